@@ -1,0 +1,248 @@
+"""Benchmark: QSA decode queries/s at 262,144 visible tokens on one MI355X.
+
+Workload (synthetic, seeded): a decode batch of 32 independent sequences, each
+with 262,144 visible tokens (65,536 complete groups, no tail), budget 512
+groups, indexer 16 heads x 128, attention 32 query heads / 4 KV heads x 128,
+F32, per-sequence slot maps = disjoint chunks of one random permutation of a
+shared 8,388,608-slot K/V pool.  One step = one qsa_decode call covering all
+eight steps of the path for the 32 rows, inputs resident in HBM.
+
+Prints one JSON line.  The roofline object describes the dominant kernel (the
+group-scoring sweep): its algorithmic bytes per launch over its mean launch
+time, measured with HIP events recorded on the launch stream inside the timed
+region.  cpu_baseline times the sequential CPU oracle on host cores over the
+same 32 rows.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA decode queries/sec at 262,144 visible tokens; achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+COUNTERS = os.path.join(ROOT, "profiles", "score_c4_counters.json")
+
+
+def algorithmic_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=128, k=512):
+    """Bytes the method must move for one decode step, by kernel."""
+    W = 4 * k  # no tail at 262,144 tokens
+    kv_row = h_kv * d * 4
+    seg = G // 16
+    chunks = math.ceil((4 * k + 3) / 64)
+    score = B * G * d_i * 4 + B * h_i * d_i * 4 + B * G * 4 + B * seg * 4
+    select = B * G * 4 + B * seg * 4 + B * (4 * k + 4) * 4 + B * 4
+    gather = B * W * 4 * 2 + B * W * 4 + 2 * B * W * kv_row + 2 * B * W * kv_row
+    attend = 2 * B * W * kv_row + B * h_q * d * 4 + B * h_q * chunks * (d + 2) * 4
+    merge = B * h_q * chunks * (d + 2) * 4 + B * h_q * (d + 1) * 4
+    return dict(score=score, select_emit=select, resolve_gather=gather, attend_chunks=attend,
+                attend_merge=merge)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("score.hip", "qsa_internal.h"):
+        with open(os.path.join(ROOT, "top_sparse_attention_qsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per score launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != source_digest():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(data, rows, threads):
+    """Oracle over the given rows: score, select, emit and resolve on host
+    copies of the pooled keys and slot maps (timed), K/V rows fetched at the
+    oracle's own slots (not timed), then the F32 online attention (timed)."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests import harness
+    s = data["spec"]
+    n = s.seq_lens[0]
+    raw = data["raw_keys"]
+    prep = []
+    for r in rows:
+        off = int(data["raw_off"][r])
+        pooled = oracle.pool_full(raw[off:off + n].cpu().numpy())
+        prep.append(dict(row=r, pooled=pooled, qi=data["index_q"][r].cpu().numpy(),
+                         smap=data["slot_map"][off:off + n].cpu().numpy(),
+                         q=data["q"][r].cpu().numpy()))
+    scale = harness.softmax_scale(s.d)
+    kv_slots = data["kv_slots"]
+
+    def phase1(p):
+        sc = oracle.score(p["qi"], p["pooled"])
+        ids = oracle.emit(oracle.select(sc, s.budget), n)
+        p["slots"] = oracle.resolve(ids, p["smap"], kv_slots)
+        return p
+
+    def phase2(p):
+        p["out"], p["lse"] = oracle.attend_online(p["q"], p["kx"], p["vx"], scale)
+        return p
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(phase1, prep))
+        t1 = time.perf_counter()
+        fetch = harness.device_kv_fetch(data["k_cache"], data["v_cache"])
+        for p in prep:
+            p["kx"], p["vx"] = fetch(p["slots"])
+        t2 = time.perf_counter()
+        list(ex.map(phase2, prep))
+        t3 = time.perf_counter()
+    timed = (t1 - t0) + (t3 - t2)
+    return dict(value=len(rows) / timed, unit="queries/s", cores=threads, kind="oracle",
+                sample=f"all {len(rows)} rows of one decode step of the same workload "
+                       f"(score+select+emit+resolve, then F32 online attention over the "
+                       f"oracle's own gathered rows; pooling and the K/V row copy untimed)",
+                seconds=timed)
+
+
+def copy_calibration(gib=1.0, reps=5):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter scale factor)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              f"multi-GPU leg (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import top_sparse_attention_qsa_amd as qsa
+    from tests import harness, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qsa.lib()  # fails loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    spec = inputs.spec("c4")
+    print(f"[bench] generating {spec.name} on cuda:0 (seed {args.seed})", file=sys.stderr,
+          flush=True)
+    data = inputs.make(spec, seed=args.seed, device="cuda")
+    case = harness.GpuCase(data)
+    rows = spec.rows
+    keep_raw = not args.no_cpu_baseline
+    if not keep_raw:
+        data["raw_keys"] = None
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        case.decode()
+    torch.cuda.synchronize()
+
+    timer = qsa.Timer(args.steps)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        case.decode(timer)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    stage = timer.read()
+    timer.close()
+    stage_ms = {name: sum(c[i] for c in stage) / len(stage)
+                for i, name in enumerate(qsa.STAGE_NAMES)}
+
+    alg = algorithmic_bytes()
+    step_bytes = sum(alg.values())
+    score_ms = stage_ms["score"]
+    achieved = alg["score"] / (score_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    widths = case.width.cpu()
+    assert int(widths.min()) == 2048 and int(widths.max()) == 2048, "unexpected widths"
+
+    result = {
+        "metric": METRIC,
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode batch of 32 sequences x 262,144 visible tokens (65,536 groups), "
+                        "budget 512 groups, indexer 16 heads x 128, attention 32 q / 4 KV heads "
+                        "x 128, shared 8,388,608-slot K/V pool, random per-sequence slot maps",
+            "batch": rows, "seq_len": spec.seq_lens[0], "budget_groups": spec.budget,
+            "index_heads": spec.h_i, "index_dim": spec.d_i, "q_heads": spec.h_q,
+            "kv_heads": spec.h_kv, "head_dim": spec.d, "kv_slots": data["kv_slots"],
+        },
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "stage_ms": stage_ms,
+        "roofline": {
+            "kernel": "score_kernel<16,128,2>",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg["score"],
+            "mean_launch_ms": score_ms,
+        },
+        "cpu_baseline": None,
+    }
+    if keep_raw:
+        threads = len(os.sched_getaffinity(0))
+        threads = max(1, min(threads, 16, rows))
+        print(f"[bench] cpu baseline: oracle over {rows} rows on {threads} threads",
+              file=sys.stderr, flush=True)
+        cb = cpu_baseline(data, list(range(rows)), threads)
+        cb.pop("seconds", None)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

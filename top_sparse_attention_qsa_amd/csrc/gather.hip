@@ -1,0 +1,82 @@
+// gather.hip -- steps 6-7: resolve each selected logical token ID once through
+// the slot map and copy only those K/V cache rows into compact scratch, in
+// row (chronological) order.  Only this step crosses from logical identity to
+// physical cache layout, so selection never needs to know whether the cache
+// wrapped, compacted or reused a slot (AFN-016 "A sparse mask is not sparse
+// attention", §Decision; §Why compact gather comes before fusion: one
+// explicit copy into bounded scratch).
+//
+// A workgroup handles kGatherTokens compact rows of one query row: the first
+// lanes resolve the slots into LDS, then all 256 threads stream the H_kv*D
+// floats of each K and V row with float4 loads and stores (2 KiB contiguous
+// per row at H_kv=4, D=128).  Out-of-range IDs or slots produce NaN rows and
+// slot -1 instead of a fault.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+__global__ void __launch_bounds__(256)
+gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__ width,
+              const int32_t* __restrict__ seq_len, const int32_t* __restrict__ slot_map,
+              const int64_t* __restrict__ slot_off, const float4* __restrict__ k_cache,
+              const float4* __restrict__ v_cache, int32_t queries, int32_t row_f4,
+              int32_t stride, int64_t kv_slots, int64_t row0, float4* __restrict__ k_out,
+              float4* __restrict__ v_out, int32_t* __restrict__ phys_slots) {
+  __shared__ int32_t slot_sh[kGatherTokens];
+  const int tid = (int)threadIdx.x;
+  const int64_t lrow = blockIdx.y;
+  const int64_t row = row0 + lrow;
+  const int32_t w = width[row];
+  const int32_t i0 = (int32_t)blockIdx.x * kGatherTokens;
+  if (w <= 0 || w > stride - 1 || i0 >= w) return;  // widths above 4k+3 are invalid
+  if (tid < kGatherTokens) {
+    const int32_t i = i0 + tid;
+    int32_t slot = -2;  // -2: past the width, nothing to copy
+    if (i < w) {
+      const int32_t b = (int32_t)(row / queries);
+      const int64_t n = (int64_t)seq_len[b] - queries + 1 + (row - (int64_t)b * queries);
+      const int32_t id = token_ids[row * stride + i];
+      slot = -1;
+      if (id >= 0 && (int64_t)id < n) {
+        const int32_t s = slot_map[slot_off[b] + id];
+        if (s >= 0 && (int64_t)s < kv_slots) slot = s;
+      }
+      if (phys_slots) phys_slots[row * stride + i] = slot;
+    }
+    slot_sh[tid] = slot;
+  }
+  __syncthreads();
+  const float nan = __int_as_float(0x7fc00000);
+  const int total = kGatherTokens * row_f4;
+  for (int e = tid; e < total; e += 256) {
+    const int t = e / row_f4;
+    const int c = e - t * row_f4;
+    const int32_t slot = slot_sh[t];
+    if (slot == -2) continue;
+    float4 kv = make_float4(nan, nan, nan, nan), vv = kv;
+    if (slot >= 0) {
+      kv = k_cache[(int64_t)slot * row_f4 + c];
+      vv = v_cache[(int64_t)slot * row_f4 + c];
+    }
+    const int64_t dst = (lrow * stride + i0 + t) * (int64_t)row_f4 + c;
+    k_out[dst] = kv;
+    v_out[dst] = vv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  const int32_t row_f4 = a.kv_heads * a.head_dim / 4;
+  dim3 grid((unsigned)((a.stride + kGatherTokens - 1) / kGatherTokens), (unsigned)a.rows);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, a.token_ids, a.width, a.seq_len,
+                     a.slot_map, a.slot_off, reinterpret_cast<const float4*>(a.k_cache),
+                     reinterpret_cast<const float4*>(a.v_cache), a.queries, row_f4, a.stride,
+                     a.kv_slots, a.row0, reinterpret_cast<float4*>(a.k_compact),
+                     reinterpret_cast<float4*>(a.v_compact), a.phys_slots);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,197 @@
+// qsa_internal.h -- device helpers and kernel launchers shared by the HIP
+// sources of libqsa.so (gfx950, wave64).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+constexpr int kWave = 64;
+constexpr int kScoreWaves = 4;        // waves per scoring workgroup
+constexpr int kScoreTilesPerWave = 2; // pooled-key tiles (64 groups each) per wave
+constexpr int kSegment = 16;          // groups per maximum used to bound the threshold
+constexpr int kSelectThreads = 1024;  // one selection workgroup per row
+constexpr int kCandCap = 4096;        // candidates kept in LDS before the streaming path
+constexpr int kGatherTokens = 8;      // compact rows per gather workgroup
+constexpr int kAttnChunk = 64;        // compact rows per attention partial
+
+// Scores are ordered through a monotone unsigned key: -0 is folded onto +0,
+// then non-negative floats get their sign bit set and negative floats are
+// bit-inverted, so unsigned comparison equals float comparison.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct RowView {
+  int64_t n;     // visible tokens
+  int64_t g;     // complete groups
+  int32_t tail;  // n mod 4
+  int32_t b;     // sequence
+  bool valid;
+};
+
+__device__ __forceinline__ RowView row_view(const int32_t* __restrict__ seq_len, int64_t row,
+                                            int32_t queries, int64_t g_max) {
+  RowView v;
+  v.b = (int32_t)(row / queries);
+  const int32_t j = (int32_t)(row - (int64_t)v.b * queries);
+  v.n = (int64_t)seq_len[v.b] - queries + 1 + j;
+  v.valid = v.n >= 0;
+  v.g = v.valid ? (v.n >> 2) : 0;
+  v.tail = v.valid ? (int32_t)(v.n & 3) : 0;
+  if (v.g > g_max) v.valid = false;
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t y = __shfl_up(v, o, kWave);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Butterfly reductions: every lane ends with the same value, reduced in a
+// fixed order independent of timing.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = v + __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Exclusive prefix sum over a whole workgroup of NT threads (NT/64 waves);
+// `wave_tot` is LDS scratch of NT/64 words.  *total receives the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* wave_tot,
+                                                        uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int wave = (int)(threadIdx.x / kWave);
+  const uint32_t inc = wave_inclusive_sum(x);
+  if (lane_id() == kWave - 1) wave_tot[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += (w < wave) ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - x;
+}
+
+// ---------------------------------------------------------------- launchers
+struct ScoreArgs {
+  const float* index_q;
+  const float* pooled;
+  const int64_t* pooled_off;
+  const int32_t* seq_len;
+  int32_t queries;
+  int64_t g_max;
+  int64_t row0;       // first global row of this launch
+  int64_t rows;       // rows in this launch
+  float* scores;      // indexed by local row
+  uint32_t* maxima;   // [rows][g_max/16] order keys, may be null
+};
+
+struct SelectArgs {
+  const float* scores;       // local rows
+  const uint32_t* maxima;    // local rows, may be null (no threshold bound)
+  const int32_t* seq_len;
+  int32_t queries;
+  int64_t g_max;
+  int32_t k;
+  int64_t row0;
+  int64_t rows;
+  uint32_t* bitmap;          // global rows, may be null
+  int32_t* token_ids;        // global rows, may be null
+  int32_t* width;            // global rows, may be null
+};
+
+struct GatherArgs {
+  const int32_t* token_ids;  // global rows
+  const int32_t* width;      // global rows
+  const int32_t* seq_len;
+  const int32_t* slot_map;
+  const int64_t* slot_off;
+  const float* k_cache;
+  const float* v_cache;
+  int32_t queries;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t stride;            // 4k+4
+  int64_t kv_slots;
+  int64_t row0;
+  int64_t rows;
+  float* k_compact;          // local rows
+  float* v_compact;
+  int32_t* phys_slots;       // global rows, may be null
+};
+
+struct AttendArgs {
+  const float* q;            // global rows
+  const float* k_compact;    // local rows
+  const float* v_compact;
+  const int32_t* width;      // global rows
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t stride;            // 4k+4
+  int32_t n_chunks;          // ceil((4k+3)/kAttnChunk)
+  float scale;
+  int64_t row0;
+  int64_t rows;
+  float* part_acc;           // [rows][H_q][n_chunks][D] local rows
+  float* part_ml;            // [rows][H_q][n_chunks][2]
+  float* out;                // global rows
+  float* lse;                // global rows, may be null
+};
+
+struct PoolArgs {
+  const float* raw_keys;
+  const int64_t* raw_off;
+  const int32_t* seq_len;
+  const int32_t* first_group;
+  float* pooled;
+  const int64_t* pooled_off;
+  int32_t batch;
+  int32_t index_dim;
+  int64_t g_max;
+};
+
+hipError_t launch_score(const ScoreArgs& a, int h_i, int d_i, hipStream_t s);
+hipError_t launch_segment_maxima(const float* scores, const int32_t* seq_len, int32_t queries,
+                                 int64_t g_max, int64_t row0, int64_t rows, uint32_t* maxima,
+                                 hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_emit(const uint32_t* bitmap, const int32_t* seq_len, int32_t queries,
+                       int64_t g_max, int32_t k, int64_t rows, int32_t* token_ids,
+                       int32_t* width, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_merge(const AttendArgs& a, hipStream_t s);
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+
+}  // namespace qsa

@@ -1,0 +1,372 @@
+// select.hip -- steps 2-5: top-k membership, chronological emission, group
+// expansion and tail append for every row.
+//
+// Membership follows the total order (score descending, group position
+// ascending); ties are settled while the set is chosen, never after it is
+// sorted (AFN-017 "Top-k chooses the set; time chooses the order", §Decision
+// and §Tie handling belongs to membership).  The chosen groups leave in
+// ascending logical position, each as four consecutive token IDs, followed
+// by the raw tail (same note, §Decision; §The dense-parity property).
+//
+// One 1024-thread workgroup per row:
+//  1. tau = the k-th largest of the per-16-group maxima (when there are at
+//     least k of them).  Those k maxima are k distinct groups scoring >= tau,
+//     so the k-th largest score is >= tau and every member scores >= tau.
+//  2. One streaming pass compacts the candidates (score >= tau) in position
+//     order into LDS.  If more than kCandCap survive (massive ties), the
+//     passes below stream the whole row from global memory instead.
+//  3. A byte-wise radix select over the order keys finds T, the k-th largest
+//     key, and the number of keys above T.
+//  4. An ordered pass keeps every key above T and the first (k - above)
+//     keys equal to T in position order -- the tie rule -- and writes each
+//     kept group at its output index, which is already chronological.
+// No sort, no float atomics; the result is unique, so it is bit-identical to
+// any correct selector.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int NT = kSelectThreads;
+constexpr int NWAVES = NT / kWave;
+
+struct SelectShared {
+  uint32_t hist[256];
+  uint32_t wave_tot[NWAVES];
+  uint32_t scal[4];
+  uint32_t cand_key[kCandCap];
+  uint32_t cand_pos[kCandCap];
+};
+
+// Histogram add in which lanes of a wavefront that share a bin are first
+// merged (up to two bins peeled per call), so a skewed digit does not
+// serialise 64 LDS atomics on one address.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const int lane = lane_id();
+  uint64_t pending = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (pending == 0) return;
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const uint32_t lb = (uint32_t)__shfl((int)bin, leader, kWave);
+    const uint64_t same = __ballot(active && bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    if ((same >> lane) & 1ull) active = false;
+    pending &= ~same;
+  }
+  if (active) atomicAdd(&hist[bin], 1u);
+}
+
+// k-th largest order key among n keys from src (1 <= k <= n) and the count of
+// keys strictly above it.  Four passes of 8 bits, most significant first.
+template <class Src>
+__device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, SelectShared& sh,
+                                  uint32_t* t_out, uint32_t* above_out) {
+  const int tid = (int)threadIdx.x;
+  uint32_t prefix = 0, mask = 0, kk = k, above = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+    const uint32_t n_up = (n + NT - 1) / NT * NT;   // whole wavefronts stay converged
+    for (uint32_t i = tid; i < n_up; i += NT) {
+      bool act = false;
+      uint32_t bin = 0;
+      if (i < n) {
+        const uint32_t key = src.key(i);
+        act = (key & mask) == prefix;
+        bin = (key >> shift) & 255u;
+      }
+      hist_add(sh.hist, bin, act);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l owns bins 4l..4l+3; find the bin holding the kk-th largest
+      const int l = tid;
+      const uint32_t h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1];
+      const uint32_t h2 = sh.hist[4 * l + 2], h3 = sh.hist[4 * l + 3];
+      const uint32_t mine = h0 + h1 + h2 + h3;
+      uint32_t suffix = mine;  // sum over lanes >= l
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)suffix, o, kWave);
+        if (l + o < kWave) suffix += y;
+      }
+      const uint32_t higher = suffix - mine;  // keys in bins above lane l's
+      if (higher < kk && kk <= suffix) {
+        uint32_t acc = higher;
+        uint32_t digit = 4u * l;
+        const uint32_t hb[4] = {h0, h1, h2, h3};
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          if (acc + hb[b] >= kk) { digit = 4u * l + b; break; }
+          acc += hb[b];
+        }
+        sh.scal[0] = digit;
+        sh.scal[1] = acc;
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = sh.scal[0], higher = sh.scal[1];
+    above += higher;
+    kk -= higher;
+    prefix |= digit << shift;
+    mask |= 255u << shift;
+  }
+  *t_out = prefix;
+  *above_out = above;
+}
+
+struct GlobalScores {
+  const float* s;
+  __device__ uint32_t key(uint32_t i) const { return order_key(s[i]); }
+};
+struct GlobalKeys {
+  const uint32_t* k;
+  __device__ uint32_t key(uint32_t i) const { return k[i]; }
+};
+struct LdsCands {
+  const uint32_t* k;
+  __device__ uint32_t key(uint32_t i) const { return k[i]; }
+};
+
+// Writes kept group g at output index o: token IDs 4g..4g+3 at 4o, and/or
+// bit g of the bitmap.
+struct Emitter {
+  int32_t* ids;        // row of 4k+4, may be null
+  uint32_t* bitmap;    // row of g_max/32 words, may be null
+  uint32_t k;
+  __device__ void keep(uint32_t o, uint32_t g) const {
+    if (ids && o < k) {
+      const int32_t t = (int32_t)(4u * g);
+      *reinterpret_cast<int4*>(ids + 4 * o) = make_int4(t, t + 1, t + 2, t + 3);
+    }
+    if (bitmap) atomicOr(&bitmap[g >> 5], 1u << (g & 31));
+  }
+};
+
+__global__ void __launch_bounds__(NT)
+select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ maxima,
+              const int32_t* __restrict__ seq_len, int32_t queries, int64_t g_max, int32_t k,
+              int64_t row0, uint32_t* __restrict__ bitmap, int32_t* __restrict__ token_ids,
+              int32_t* __restrict__ width) {
+  __shared__ SelectShared sh;
+  const int tid = (int)threadIdx.x;
+  const int64_t lrow = blockIdx.x;
+  const int64_t row = row0 + lrow;
+  const RowView rv = row_view(seq_len, row, queries, g_max);
+  const int32_t stride = 4 * k + 4;
+  int32_t* ids = token_ids ? token_ids + row * stride : nullptr;
+  uint32_t* bm = bitmap ? bitmap + row * (g_max / 32) : nullptr;
+
+  if (bm) {
+    const int64_t words = g_max / 32;
+    for (int64_t w = tid; w < words; w += NT) bm[w] = 0u;
+    __threadfence();
+    __syncthreads();
+  }
+  if (!rv.valid) {
+    if (ids)
+      for (int i = tid; i < stride; i += NT) ids[i] = -1;
+    if (width && tid == 0) width[row] = -1;
+    return;
+  }
+
+  const uint32_t G = (uint32_t)rv.g;
+  const Emitter em{ids, bm, (uint32_t)k};
+  uint32_t kept;
+  if (G <= (uint32_t)k) {
+    // every complete group survives: the dense causal row
+    for (uint32_t g = tid; g < G; g += NT) em.keep(g, g);
+    kept = G;
+  } else {
+    const float* __restrict__ srow = scores + lrow * g_max;
+    // 1. threshold bound from the segment maxima
+    uint32_t tau = 0;
+    const uint32_t segs = (G + kSegment - 1) / kSegment;
+    if (maxima && segs >= (uint32_t)k) {
+      uint32_t above_unused;
+      radix_kth_largest(GlobalKeys{maxima + lrow * (g_max / kSegment)}, segs, (uint32_t)k, sh,
+                        &tau, &above_unused);
+    }
+    // 2. ordered candidate compaction: 16 consecutive positions per thread
+    uint32_t n_cand = 0;
+    bool overflow = false;
+    for (uint32_t base = 0; base < G; base += 16u * NT) {
+      const uint32_t p0 = base + 16u * tid;
+      uint32_t keys[16];
+      uint32_t flags = 0;
+      if (p0 + 16 <= G) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 f = *reinterpret_cast<const float4*>(srow + p0 + 4 * v);
+          keys[4 * v + 0] = order_key(f.x);
+          keys[4 * v + 1] = order_key(f.y);
+          keys[4 * v + 2] = order_key(f.z);
+          keys[4 * v + 3] = order_key(f.w);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) keys[e] = (p0 + e < G) ? order_key(srow[p0 + e]) : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (p0 + e < G && keys[e] >= tau) flags |= 1u << e;
+      uint32_t tot;
+      const uint32_t off = block_exclusive_sum<NT>((uint32_t)__popc(flags), sh.wave_tot, &tot);
+      if (n_cand + tot > (uint32_t)kCandCap) { overflow = true; break; }
+      uint32_t o = n_cand + off;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((flags >> e) & 1u) { sh.cand_key[o] = keys[e]; sh.cand_pos[o] = p0 + e; ++o; }
+      n_cand += tot;
+    }
+    __syncthreads();
+
+    // 3. exact k-th largest key and the count above it
+    uint32_t T, above;
+    const uint32_t n_src = overflow ? G : n_cand;
+    if (overflow)
+      radix_kth_largest(GlobalScores{srow}, G, (uint32_t)k, sh, &T, &above);
+    else
+      radix_kth_largest(LdsCands{sh.cand_key}, n_cand, (uint32_t)k, sh, &T, &above);
+    const uint32_t need = (uint32_t)k - above;  // keys equal to T to keep, lowest positions first
+
+    // 4. ordered keep pass: 4 consecutive entries per thread per round
+    uint32_t out_base = 0, eq_base = 0;
+    for (uint32_t base = 0; base < n_src; base += 4u * NT) {
+      const uint32_t i0 = base + 4u * tid;
+      uint32_t key[4], pos[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = i0 + e;
+        if (i < n_src) {
+          key[e] = overflow ? order_key(srow[i]) : sh.cand_key[i];
+          pos[e] = overflow ? i : sh.cand_pos[i];
+        } else {
+          key[e] = 0u;
+          pos[e] = 0u;
+        }
+      }
+      uint32_t eq_flags = 0, gt_flags = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (i0 + e < n_src) {
+          eq_flags |= (key[e] == T ? 1u : 0u) << e;
+          gt_flags |= (key[e] > T ? 1u : 0u) << e;
+        }
+      }
+      uint32_t eq_tot;
+      uint32_t eq_rank = eq_base + block_exclusive_sum<NT>((uint32_t)__popc(eq_flags),
+                                                           sh.wave_tot, &eq_tot);
+      uint32_t keep_flags = gt_flags;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((eq_flags >> e) & 1u) {
+          if (eq_rank < need) keep_flags |= 1u << e;
+          ++eq_rank;
+        }
+      uint32_t keep_tot;
+      uint32_t o = out_base + block_exclusive_sum<NT>((uint32_t)__popc(keep_flags),
+                                                      sh.wave_tot, &keep_tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((keep_flags >> e) & 1u) em.keep(o++, pos[e]);
+      out_base += keep_tot;
+      eq_base += eq_tot;
+    }
+    kept = out_base;  // == k
+  }
+
+  // 5. raw tail, width and padding
+  if (ids) {
+    const int32_t body = 4 * (int32_t)kept;
+    const int32_t w = body + rv.tail;
+    for (int i = body + tid; i < stride; i += NT)
+      ids[i] = (i < w) ? (int32_t)(4 * rv.g + (i - body)) : -1;
+  }
+  if (width && tid == 0) width[row] = 4 * (int32_t)kept + rv.tail;
+}
+
+// Bitmap -> chronological token IDs: popcount prefix over the words in order.
+__global__ void __launch_bounds__(NT)
+emit_kernel(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ seq_len,
+            int32_t queries, int64_t g_max, int32_t k, int32_t* __restrict__ token_ids,
+            int32_t* __restrict__ width) {
+  __shared__ uint32_t wave_tot[NWAVES];
+  const int tid = (int)threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const RowView rv = row_view(seq_len, row, queries, g_max);
+  const int32_t stride = 4 * k + 4;
+  int32_t* ids = token_ids + row * stride;
+  if (!rv.valid) {
+    for (int i = tid; i < stride; i += NT) ids[i] = -1;
+    if (tid == 0) width[row] = -1;
+    return;
+  }
+  const uint32_t* bm = bitmap + row * (g_max / 32);
+  const uint32_t G = (uint32_t)rv.g;
+  const uint32_t words = (G + 31) / 32;
+  uint32_t total = 0;
+  for (uint32_t base = 0; base < words; base += 4u * NT) {
+    const uint32_t w0 = base + 4u * tid;
+    uint32_t wv[4];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = w0 + e;
+      uint32_t v = (w < words) ? bm[w] : 0u;
+      if (w == words - 1 && (G & 31)) v &= (1u << (G & 31)) - 1u;  // bits past G
+      wv[e] = v;
+      cnt += (uint32_t)__popc(v);
+    }
+    uint32_t tot;
+    uint32_t o = total + block_exclusive_sum<NT>(cnt, wave_tot, &tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t v = wv[e];
+      while (v) {
+        const uint32_t bit = (uint32_t)__ffs(v) - 1u;
+        v &= v - 1u;
+        if (o < (uint32_t)k) {
+          const int32_t t = (int32_t)(4u * (32u * (w0 + e) + bit));
+          *reinterpret_cast<int4*>(ids + 4 * o) = make_int4(t, t + 1, t + 2, t + 3);
+        }
+        ++o;
+      }
+    }
+    total += tot;
+  }
+  __syncthreads();
+  if (total > (uint32_t)k) {
+    // more groups than the budget: not a selection this row can hold
+    for (int i = tid; i < stride; i += NT) ids[i] = -1;
+    if (tid == 0) width[row] = -1;
+    return;
+  }
+  const int32_t body = 4 * (int32_t)total;
+  const int32_t w = body + rv.tail;
+  for (int i = body + tid; i < stride; i += NT)
+    ids[i] = (i < w) ? (int32_t)(4 * rv.g + (i - body)) : -1;
+  if (tid == 0) width[row] = w;
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.rows), dim3(NT), 0, s, a.scores, a.maxima,
+                     a.seq_len, a.queries, a.g_max, a.k, a.row0, a.bitmap, a.token_ids,
+                     a.width);
+  return hipGetLastError();
+}
+
+hipError_t launch_emit(const uint32_t* bitmap, const int32_t* seq_len, int32_t queries,
+                       int64_t g_max, int32_t k, int64_t rows, int32_t* token_ids,
+                       int32_t* width, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)rows), dim3(NT), 0, s, bitmap, seq_len, queries,
+                     g_max, k, token_ids, width);
+  return hipGetLastError();
+}
+
+}  // namespace qsa
