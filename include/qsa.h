@@ -86,7 +86,7 @@ typedef struct qsa_shape {
     int32_t budget_groups;  /* k, groups kept per row ([SET] §Decision: 512)        */
     int64_t max_groups;     /* G_max >= G of every row, a multiple of 64: the      */
                             /* stride of score rows                                 */
-    int64_t kv_slots;       /* S, physical slots of the K/V cache                   */
+    int64_t kv_slots;       /* S >= 1, physical slots of the K/V cache              */
     int32_t rows_in_flight; /* qsa_decode only: rows per pass, bounding the         */
                             /* workspace; 0 = all rows in one pass                  */
     int32_t reserved;       /* must be 0                                            */

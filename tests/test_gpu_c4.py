@@ -1,0 +1,62 @@
+"""Full-size decode parity: 32 sequences x 262,144 visible tokens, budget 512,
+indexer 16 x 128, attention 32 q / 4 KV x 128, shared 8,388,608-slot K/V pool
+-- the workload and launch configuration bench.py times.
+
+The oracle recomputes sampled rows end to end from host copies of the same
+generated inputs (K/V rows fetched at the oracle's own resolved slots);
+every row is checked against properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests import harness, inputs
+
+pytestmark = pytest.mark.gpu
+
+SAMPLED_ROWS = (0, 13, 31)
+
+
+@pytest.fixture(scope="module")
+def c4():
+    data = inputs.make(inputs.spec("c4"), seed=2, device="cuda")
+    case = harness.GpuCase(data)
+    case.decode()
+    torch.cuda.synchronize()
+    return case
+
+
+def test_c4_sampled_rows_match_oracle(c4):
+    ids = c4.token_ids.cpu().numpy()
+    width = c4.width.cpu().numpy()
+    out = c4.out.cpu().numpy()
+    lse = c4.lse.cpu().numpy()
+    fetch = harness.device_kv_fetch(c4.k_cache, c4.v_cache)
+    for r in SAMPLED_ROWS:
+        exp = harness.oracle_row(c4.data, r, kv_fetch=fetch)
+        assert width[r] == 2048
+        assert np.array_equal(ids[r, :2048], exp["ids"]), r
+        err = harness.normwise_rel_err(out[r], exp["out_exact"])
+        assert err <= 2e-6, (r, err)
+        assert np.allclose(lse[r], exp["lse_exact"], rtol=0, atol=1e-5)
+
+
+def test_c4_all_rows_structural(c4):
+    """Every row: width 4k, strictly ascending group-aligned runs of four, no
+    tail (262,144 = 4 x 65,536), -1 padding, finite outputs."""
+    ids = c4.token_ids.cpu().numpy()
+    assert np.all(c4.width.cpu().numpy() == 2048)
+    body = ids[:, :2048].reshape(32, 512, 4)
+    assert np.all(body[:, :, 0] % 4 == 0)
+    assert np.all(body - body[:, :, :1] == np.arange(4))
+    assert np.all(np.diff(body[:, :, 0], axis=1) > 0)
+    assert np.all(ids[:, 2048:] == -1)
+    assert torch.isfinite(c4.out).all() and torch.isfinite(c4.lse).all()
+
+
+def test_c4_repeat_is_bitwise_identical(c4):
+    ref = (c4.token_ids.clone(), c4.out.clone(), c4.lse.clone())
+    c4.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], c4.token_ids)
+    assert torch.equal(ref[1], c4.out) and torch.equal(ref[2], c4.lse)

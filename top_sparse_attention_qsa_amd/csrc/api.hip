@@ -59,7 +59,7 @@ int validate(const qsa_shape* s, int need) {
     if (!is_pow2_in(s->q_heads / s->kv_heads, 1, 16)) return QSA_ERR_UNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return QSA_ERR_UNSUPPORTED;
     if (s->kv_heads > 65535) return QSA_ERR_UNSUPPORTED;
-    if (s->kv_slots < 0 || s->kv_slots > INT32_MAX) return QSA_ERR_SHAPE;
+    if (s->kv_slots < 1 || s->kv_slots > INT32_MAX) return QSA_ERR_SHAPE;
   }
   return QSA_OK;
 }

@@ -11,12 +11,16 @@
 // in ascending chunk order (running maximum, rescale, denominator and
 // accumulator updates).  No float atomics: results are run-to-run identical.
 //
-// attend_chunk_kernel: one workgroup per (chunk, KV head, row) stages the
-// chunk's K and V rows of that KV head in LDS (K rows padded by 16 bytes so
-// lane-per-row float4 reads are bank-conflict free) and serves every query
-// head of its GQA group (query head hq reads KV head hq / (H_q/H_kv)).
-// Scores: lane = compact row, query from scalar loads.  P.V: lane = output
-// dimension.  merge_kernel: one wavefront per (query head, row).
+// attend_chunk_kernel: one workgroup per (chunk, KV head, row) serves every
+// query head of the KV head's GQA group (query head hq reads KV head
+// hq / (H_q/H_kv)).  Scores: the chunk's K rows are staged in LDS (rows padded
+// by 16 bytes so lane-per-row float4 reads are bank-conflict free), lane =
+// compact row, query from scalar loads.  P.V: wavefront w accumulates rows
+// [w*C/NW, (w+1)*C/NW) in row order with lane = output dimension, reading its
+// V rows straight from memory (issued before the score phase); the NW
+// partial sums are then added in wavefront order.  The chunk's accumulation
+// order is therefore fixed by the chunk alone.  merge_kernel: four
+// wavefronts per (query head, row).
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -25,126 +29,236 @@ namespace {
 constexpr int C = kAttnChunk;
 
 template <int D, int GQ>
+struct AttnCfg {
+  static constexpr int NW = GQ < 4 ? GQ : 4;
+  static constexpr int NT = NW * kWave;
+  static constexpr int HPW = GQ / NW;    // query heads per wavefront in the score phase
+  static constexpr int KPW = C / NW;     // compact rows per wavefront in the P.V phase
+  static constexpr int KP = D + 4;       // padded K row, floats
+  static constexpr int DPL = D / kWave;  // output dims per lane
+  static constexpr int KV4 = C * D / 4 / NT;  // K float4 per thread per chunk
+  static constexpr int KFLOATS = C * KP;
+  static constexpr int RFLOATS = NW * GQ * D;  // per-wavefront P.V partials, aliasing K
+  static constexpr int SFLOATS = KFLOATS > RFLOATS ? KFLOATS : RFLOATS;
+};
+
+// Work item it -> (chunk, local row, KV head), chunk-major, so that the items
+// of one chunk index are consecutive and a launch whose grid divides the item
+// count of the non-empty chunks gives every workgroup the same amount of work.
+struct Item {
+  int chunk;
+  int hk;
+  int64_t lrow;
+};
+__device__ __forceinline__ Item item_of(int64_t it, int64_t rows, int kv_heads) {
+  Item x;
+  const int64_t per_chunk = rows * kv_heads;
+  x.chunk = (int)(it / per_chunk);
+  const int64_t r = it - (int64_t)x.chunk * per_chunk;
+  x.lrow = r / kv_heads;
+  x.hk = (int)(r - x.lrow * kv_heads);
+  return x;
+}
+
+template <int D, int GQ>
 __global__ void __launch_bounds__((GQ < 4 ? GQ : 4) * kWave)
 attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_compact,
                     const float* __restrict__ v_compact, const int32_t* __restrict__ width,
                     int32_t q_heads, int32_t kv_heads, int32_t stride, int32_t n_chunks,
-                    float scale, int64_t row0, float* __restrict__ part_acc,
+                    float scale, int64_t row0, int64_t rows, float* __restrict__ part_acc,
                     float* __restrict__ part_ml) {
-  constexpr int NW = GQ < 4 ? GQ : 4;
-  constexpr int HPW = GQ / NW;   // query heads per wavefront
-  constexpr int KP = D + 4;      // padded K row, floats
-  constexpr int DPL = D / kWave; // output dims per lane
-  __shared__ float4 ks4[C * KP / 4];
-  __shared__ float4 vs4[C * D / 4];
-  __shared__ float ps[GQ * C];
-  const float* ks = reinterpret_cast<const float*>(ks4);
-  const float* vs = reinterpret_cast<const float*>(vs4);
+  using A = AttnCfg<D, GQ>;
+  constexpr int NW = A::NW, NT = A::NT, HPW = A::HPW, KPW = A::KPW, KP = A::KP;
+  constexpr int DPL = A::DPL, KV4 = A::KV4;
+  __shared__ float4 smem4[A::SFLOATS / 4];
+  __shared__ float4 ps4[GQ * C / 4];
+  float* smem = reinterpret_cast<float*>(smem4);
+  float* ps = reinterpret_cast<float*>(ps4);
 
   const int tid = (int)threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = wave_id();
   const int lane = lane_id();
-  const int chunk = (int)blockIdx.x;
-  const int hk = (int)blockIdx.y;
-  const int64_t lrow = blockIdx.z;
-  const int64_t row = row0 + lrow;
-  const int32_t w = width[row];
-  const int32_t c0 = chunk * C;
-  if (w <= 0 || w > stride - 1 || c0 >= w) return;  // widths above 4k+3 are invalid
-  const int cn = (w - c0) < C ? (w - c0) : C;
-
-  // stage K and V of this chunk (rows past the width are zero)
+  const int64_t items = (int64_t)n_chunks * rows * kv_heads;
   const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact rows
-  const float* kb = k_compact + ((lrow * stride + c0) * kv_heads + hk) * (int64_t)D;
-  const float* vb = v_compact + ((lrow * stride + c0) * kv_heads + hk) * (int64_t)D;
-  for (int e = tid; e < C * D / 4; e += NW * kWave) {
-    const int i = e / (D / 4);
-    const int c = e - i * (D / 4);
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-    if (i < cn) {
-      kv = *reinterpret_cast<const float4*>(kb + i * rstride + 4 * c);
-      vv = *reinterpret_cast<const float4*>(vb + i * rstride + 4 * c);
-    }
-    ks4[(i * KP) / 4 + c] = kv;
-    vs4[e] = vv;
-  }
-  __syncthreads();
 
-  // scores for this wavefront's query heads: lane = compact row
-  const float* qrow[HPW];
+  // Every load is unconditional: rows past a chunk's width read the chunk's
+  // last valid row (always in bounds); their K rows are zeroed in LDS and
+  // their weights p are 0, so they add nothing.  No load sits behind a branch.
+  // Prefetches are unconditional as well: an empty or out-of-range next item
+  // loads (and ignores) row 0 of the last item's chunk, which always exists.
+  auto chunk_rows = [&](const Item& x) -> int {  // rows of this chunk, 0 = no work
+    const int32_t w = width[row0 + x.lrow];
+    const int c0 = x.chunk * C;
+    if (w <= 0 || w > stride - 1 || c0 >= w) return 0;
+    return (w - c0) < C ? (w - c0) : C;
+  };
+  auto base_of = [&](const float* base, const Item& x) -> const float* {
+    return base + ((x.lrow * stride + (int64_t)x.chunk * C) * kv_heads + x.hk) * (int64_t)D;
+  };
+  float4 kst[KV4];
+  float vreg[KPW][DPL];
+  auto load_k = [&](const Item& x, int cn_raw) {
+    const int cn = cn_raw > 0 ? cn_raw : 1;
+    const float* kb = base_of(k_compact, x);
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-    qrow[hh] = q + (row * q_heads + (int64_t)hk * GQ + wave * HPW + hh) * D;
-  float dot[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) dot[hh] = 0.0f;
-#pragma unroll 8
-  for (int d = 0; d < D; d += 4) {
-    const float4 k4 = *reinterpret_cast<const float4*>(ks + lane * KP + d);
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float a = dot[hh];
-      a = __builtin_fmaf(qrow[hh][d + 0], k4.x, a);
-      a = __builtin_fmaf(qrow[hh][d + 1], k4.y, a);
-      a = __builtin_fmaf(qrow[hh][d + 2], k4.z, a);
-      a = __builtin_fmaf(qrow[hh][d + 3], k4.w, a);
-      dot[hh] = a;
+    for (int r = 0; r < KV4; ++r) {
+      const int e = tid + r * NT;
+      const int i = e / (D / 4);
+      const int c = e - i * (D / 4);
+      const int ic = i < cn ? i : cn - 1;
+      kst[r] = *reinterpret_cast<const float4*>(kb + ic * rstride + 4 * c);
     }
-  }
-  float m_h[HPW], l_h[HPW];
+  };
+  auto load_v = [&](const Item& x, int cn_raw) {
+    const int cn = cn_raw > 0 ? cn_raw : 1;
+    const float* vb = base_of(v_compact, x);
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const float s = (lane < cn) ? dot[hh] * scale : -INFINITY;
-    const float m = wave_max(s);
-    const float p = (lane < cn) ? expf(s - m) : 0.0f;
-    m_h[hh] = m;
-    l_h[hh] = wave_sum(p);
-    ps[(wave * HPW + hh) * C + lane] = p;
-  }
-  __syncthreads();
+    for (int j = 0; j < KPW; ++j) {
+      const int i = wave * KPW + j;
+      const int ic = i < cn ? i : cn - 1;
+      if constexpr (DPL == 2) {
+        const float2 v2 = *reinterpret_cast<const float2*>(vb + ic * rstride + 2 * lane);
+        vreg[j][0] = v2.x;
+        vreg[j][1] = v2.y;
+      } else {
+        vreg[j][0] = vb[ic * rstride + lane];
+      }
+    }
+  };
 
-  // P.V: lane owns dims lane*DPL .. lane*DPL+DPL-1; rows in chronological order
-  float acc[HPW][DPL];
+  int64_t it = blockIdx.x;
+  Item cur = item_of(it < items ? it : items - 1, rows, kv_heads);
+  int cn = it < items ? chunk_rows(cur) : 0;
+  load_k(cur, cn);
+  load_v(cur, cn);
+  while (it < items) {
+    const int64_t it_next = it + gridDim.x;
+    const Item nxt = item_of(it_next < items ? it_next : items - 1, rows, kv_heads);
+    const int cn_next = it_next < items ? chunk_rows(nxt) : 0;
+    // An item with no rows (cn == 0) runs the same code on masked rows and
+    // skips its stores, so every prefetch is issued from one program point.
+    {
+      // stage this item's K in LDS (rows past the width are zero)
+      __syncthreads();  // the previous item is done with LDS
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
+      for (int r = 0; r < KV4; ++r) {
+        const int e = tid + r * NT;
+        const int i = e / (D / 4);
+        const int c = e - i * (D / 4);
+        smem4[(i * KP) / 4 + c] = i < cn ? kst[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+      // next item's K streams in under this item; the scheduling barriers keep
+      // the compiler from hoisting it (or V below) above the last use of the
+      // registers it refills, which would double the register footprint
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(nxt, cn_next);
+
+      // scores for this wavefront's query heads: lane = compact row
+      const int64_t row = row0 + cur.lrow;
+      const float* qrow[HPW];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[hh][j] = 0.0f;
+      for (int hh = 0; hh < HPW; ++hh)
+        qrow[hh] = q + (row * q_heads + (int64_t)cur.hk * GQ + wave * HPW + hh) * D;
+      float dot[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) dot[hh] = 0.0f;
 #pragma unroll 4
-  for (int i = 0; i < C; ++i) {
-    float v[DPL];
-    if constexpr (DPL == 2) {
-      const float2 v2 = *reinterpret_cast<const float2*>(vs + i * D + 2 * lane);
-      v[0] = v2.x;
-      v[1] = v2.y;
-    } else {
-      v[0] = vs[i * D + lane];
+      for (int d = 0; d < D; d += 4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(smem + lane * KP + d);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          float a = dot[hh];
+          a = __builtin_fmaf(qrow[hh][d + 0], k4.x, a);
+          a = __builtin_fmaf(qrow[hh][d + 1], k4.y, a);
+          a = __builtin_fmaf(qrow[hh][d + 2], k4.z, a);
+          a = __builtin_fmaf(qrow[hh][d + 3], k4.w, a);
+          dot[hh] = a;
+        }
+      }
+      const int64_t slot0 = (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_chunks + cur.chunk;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float sc = (lane < cn) ? dot[hh] * scale : -INFINITY;
+        const float m = wave_max(sc);
+        const float p = (lane < cn) ? expf(sc - m) : 0.0f;
+        const float l = wave_sum(p);
+        ps[(wave * HPW + hh) * C + lane] = p;
+        if (lane == 0 && cn > 0)
+          *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)(wave * HPW + hh) * n_chunks) * 2) =
+              make_float2(m, l);
+      }
+      __syncthreads();  // ps complete; K no longer read, so smem can hold partials
+
+      // P.V over this wavefront's rows, in row order; lane owns dims lane*DPL..
+      float acc[GQ][DPL];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) acc[h][t] = 0.0f;
+      // head-major, one head's weights live at a time (the scheduling barrier
+      // keeps the compiler from hoisting every head's LDS reads at once)
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        float4 p4[KPW / 4];
+#pragma unroll
+        for (int j4 = 0; j4 < KPW / 4; ++j4) p4[j4] = ps4[(h * C + wave * KPW) / 4 + j4];
+#pragma unroll
+        for (int j4 = 0; j4 < KPW / 4; ++j4) {
+          const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
+              acc[h][t] = __builtin_fmaf(pv[jj], vreg[4 * j4 + jj][t], acc[h][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(nxt, cn_next);  // next item's V streams in under the rest
+
+      // combine the wavefronts' partial sums in wavefront order
+      if constexpr (NW == 1) {
+        if (cn > 0)
+#pragma unroll
+          for (int h = 0; h < GQ; ++h)
+#pragma unroll
+            for (int t = 0; t < DPL; ++t)
+              part_acc[(slot0 + (int64_t)h * n_chunks) * D + lane * DPL + t] = acc[h][t];
+      } else {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h)
+#pragma unroll
+          for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
+        __syncthreads();
+        for (int o = tid; o < (cn > 0 ? GQ * D : 0); o += NT) {
+          const int h = o / D;
+          const int d = o - h * D;
+          float sum = smem[h * D + d];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) sum = sum + smem[(ww * GQ + h) * D + d];
+          part_acc[(slot0 + (int64_t)h * n_chunks) * D + d] = sum;
+        }
+      }
     }
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float p = ps[(wave * HPW + hh) * C + i];
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[hh][j] = __builtin_fmaf(p, v[j], acc[hh][j]);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const int64_t hq = (int64_t)hk * GQ + wave * HPW + hh;
-    const int64_t slot = (lrow * q_heads + hq) * n_chunks + chunk;
-    float* pa = part_acc + slot * D;
-    if constexpr (DPL == 2)
-      *reinterpret_cast<float2*>(pa + 2 * lane) = make_float2(acc[hh][0], acc[hh][1]);
-    else
-      pa[lane] = acc[hh][0];
-    if (lane == 0) *reinterpret_cast<float2*>(part_ml + slot * 2) = make_float2(m_h[hh], l_h[hh]);
+    it = it_next;
+    cur = nxt;
+    cn = cn_next;
   }
 }
 
+// Merge of the chunk partials of one (query head, row): lane c holds chunk
+// c's (m_c, l_c) and its weight a_c = exp(m_c - m); four wavefronts each fold
+// a contiguous quarter of the chunks in ascending order (weights broadcast
+// from their lanes), then the quarters are added in order.
 template <int D>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(4 * kWave)
 merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_ml,
              const int32_t* __restrict__ width, int32_t q_heads, int32_t n_chunks,
              int32_t stride, int64_t row0, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int DPL = D / kWave;
+  __shared__ float red[4][D + 1];
+  const int wave = wave_id();
   const int lane = lane_id();
   const int64_t hq = blockIdx.x;
   const int64_t lrow = blockIdx.y;
@@ -152,40 +266,95 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
   const int32_t w = width[row];
   float* o = out + (row * q_heads + hq) * D;
   if (w <= 0 || w > stride - 1) {
-    const float fill = (w == 0) ? 0.0f : __int_as_float(0x7fc00000);
+    if (wave == 0) {
+      const float fill = (w == 0) ? 0.0f : __int_as_float(0x7fc00000);
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[lane * DPL + j] = fill;
-    if (lse && lane == 0) lse[row * q_heads + hq] = (w == 0) ? -INFINITY : fill;
+      for (int j = 0; j < DPL; ++j) o[lane * DPL + j] = fill;
+      if (lse && lane == 0) lse[row * q_heads + hq] = (w == 0) ? -INFINITY : fill;
+    }
     return;
   }
   const int nc = (w + C - 1) / C;
   const int64_t base = (lrow * q_heads + hq) * n_chunks;
-  float m = -INFINITY;
-  for (int c = 0; c < nc; ++c) m = fmaxf(m, part_ml[(base + c) * 2]);
+  // the running maximum over all chunks (every wavefront computes it)
+  float mx = -INFINITY;
+  for (int c = lane; c < nc; c += kWave) mx = fmaxf(mx, part_ml[(base + c) * 2]);
+  const float m = wave_max(mx);
+  const int per = (nc + 3) / 4;
+  const int cb = wave * per;
+  const int ce = (cb + per) < nc ? (cb + per) : nc;
   float l = 0.0f;
   float acc[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (base + c) * 2);
-    const float a = expf(ml.x - m);
-    l = __builtin_fmaf(ml.y, a, l);
-    const float* pa = part_acc + (base + c) * D + lane * DPL;
+  for (int c0 = cb; c0 < ce; c0 += kWave) {
+    // lane t of this batch holds chunk c0+t's weight and weighted denominator
+    const int cl = c0 + lane;
+    float a_l = 0.0f, wl_l = 0.0f;
+    if (cl < ce) {
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + (base + cl) * 2);
+      a_l = expf(ml.x - m);
+      wl_l = ml.y * a_l;
+    }
+    const int cnt = (ce - c0) < kWave ? (ce - c0) : kWave;
+#pragma unroll 8
+    for (int t = 0; t < cnt; ++t) {
+      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_l), t));
+      l = l + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl_l), t));
+      const float* pa = part_acc + (base + c0 + t) * D + lane * DPL;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[j] = __builtin_fmaf(pa[j], a, acc[j]);
+      for (int j = 0; j < DPL; ++j) acc[j] = __builtin_fmaf(pa[j], a, acc[j]);
+    }
   }
 #pragma unroll
-  for (int j = 0; j < DPL; ++j) o[lane * DPL + j] = acc[j] / l;
-  if (lse && lane == 0) lse[row * q_heads + hq] = m + logf(l);
+  for (int j = 0; j < DPL; ++j) red[wave][lane * DPL + j] = acc[j];
+  if (lane == 0) red[wave][D] = l;
+  __syncthreads();
+  if (wave == 0) {
+    float lt = red[0][D];
+    float at[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) at[j] = red[0][lane * DPL + j];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      lt = lt + red[ww][D];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) at[j] = at[j] + red[ww][lane * DPL + j];
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[lane * DPL + j] = at[j] / lt;
+    if (lse && lane == 0) lse[row * q_heads + hq] = m + logf(lt);
+  }
+}
+
+// Persistent launch: as many workgroups as can be resident at once (queried
+// once per kernel instance), each walking the work items with a stride of the
+// grid size.
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
 }
 
 template <int D, int GQ>
 hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
-  constexpr int NW = GQ < 4 ? GQ : 4;
-  dim3 grid((unsigned)a.n_chunks, (unsigned)a.kv_heads, (unsigned)a.rows);
-  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ>), grid, dim3(NW * kWave), 0, s, a.q,
+  using A = AttnCfg<D, GQ>;
+  static int per_cu = 0;  // resident workgroups per compute unit for this instance
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ>, A::NT, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int64_t items = (int64_t)a.n_chunks * a.rows * a.kv_heads;
+  const int64_t slots = (int64_t)device_cus() * per_cu;
+  const unsigned grid = (unsigned)(items < slots ? items : slots);
+  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ>), dim3(grid), dim3(A::NT), 0, s, a.q,
                      a.k_compact, a.v_compact, a.width, a.q_heads, a.kv_heads, a.stride,
-                     a.n_chunks, a.scale, a.row0, a.part_acc, a.part_ml);
+                     a.n_chunks, a.scale, a.row0, a.rows, a.part_acc, a.part_ml);
   return hipGetLastError();
 }
 
@@ -217,11 +386,11 @@ hipError_t launch_merge(const AttendArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.q_heads, (unsigned)a.rows);
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kWave), 0, s, a.part_acc, a.part_ml,
+      hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(4 * kWave), 0, s, a.part_acc, a.part_ml,
                          a.width, a.q_heads, a.n_chunks, a.stride, a.row0, a.out, a.lse);
       break;
     case 128:
-      hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kWave), 0, s, a.part_acc, a.part_ml,
+      hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(4 * kWave), 0, s, a.part_acc, a.part_ml,
                          a.width, a.q_heads, a.n_chunks, a.stride, a.row0, a.out, a.lse);
       break;
     default: return hipErrorInvalidValue;

@@ -47,21 +47,42 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
     slot_sh[tid] = slot;
   }
   __syncthreads();
+  // All loads of a thread are issued before any store (slots that are out of
+  // range or past the width read slot 0 and are masked afterwards), so the
+  // copy is one memory round trip per workgroup, not one per float4.
+  // All loads of a pass are issued before any store (slots that are out of
+  // range or past the width read slot 0, which exists because kv_slots >= 1,
+  // and are masked afterwards), so each pass costs one memory round trip.
   const float nan = __int_as_float(0x7fc00000);
   const int total = kGatherTokens * row_f4;
-  for (int e = tid; e < total; e += 256) {
-    const int t = e / row_f4;
-    const int c = e - t * row_f4;
-    const int32_t slot = slot_sh[t];
-    if (slot == -2) continue;
-    float4 kv = make_float4(nan, nan, nan, nan), vv = kv;
-    if (slot >= 0) {
-      kv = k_cache[(int64_t)slot * row_f4 + c];
-      vv = v_cache[(int64_t)slot * row_f4 + c];
+  constexpr int kPer = 8;  // float4 per thread per pass
+  for (int base = 0; base < total; base += kPer * 256) {
+    float4 kv[kPer], vv[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int e0 = base + tid + r * 256;
+      const int e = e0 < total ? e0 : total - 1;  // branch-free: the tail re-reads the last float4
+      const int t = e / row_f4;
+      const int c = e - t * row_f4;
+      const int32_t slot = slot_sh[t];
+      const int64_t src = (int64_t)(slot >= 0 ? slot : 0) * row_f4 + c;
+      kv[r] = k_cache[src];
+      vv[r] = v_cache[src];
     }
-    const int64_t dst = (lrow * stride + i0 + t) * (int64_t)row_f4 + c;
-    k_out[dst] = kv;
-    v_out[dst] = vv;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int e = base + tid + r * 256;
+      if (e < total) {
+        const int t = e / row_f4;
+        const int c = e - t * row_f4;
+        const int32_t slot = slot_sh[t];
+        if (slot != -2) {
+          const int64_t dst = (lrow * stride + i0 + t) * (int64_t)row_f4 + c;
+          k_out[dst] = slot >= 0 ? kv[r] : make_float4(nan, nan, nan, nan);
+          v_out[dst] = slot >= 0 ? vv[r] : make_float4(nan, nan, nan, nan);
+        }
+      }
+    }
   }
 }
 

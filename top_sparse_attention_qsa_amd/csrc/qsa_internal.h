@@ -10,8 +10,7 @@
 namespace qsa {
 
 constexpr int kWave = 64;
-constexpr int kScoreWaves = 4;        // waves per scoring workgroup
-constexpr int kScoreTilesPerWave = 2; // pooled-key tiles (64 groups each) per wave
+constexpr int kScoreWaves = 4;        // waves (one 64-group tile each) per scoring workgroup
 constexpr int kSegment = 16;          // groups per maximum used to bound the threshold
 constexpr int kSelectThreads = 1024;  // one selection workgroup per row
 constexpr int kCandCap = 4096;        // candidates kept in LDS before the streaming path
@@ -49,6 +48,12 @@ __device__ __forceinline__ RowView row_view(const int32_t* __restrict__ seq_len,
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Index of this wavefront within its workgroup, as a value the compiler knows
+// to be uniform (so addresses derived from it use scalar loads).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {

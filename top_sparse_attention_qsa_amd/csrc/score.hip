@@ -7,10 +7,9 @@
 // scores are bit-reproducible and equal ties stay equal wherever a group
 // falls in a tile.
 //
-// Mapping: one lane owns one group.  A wavefront owns kScoreTilesPerWave
-// pooled-key tiles of 64 groups; in the tiled layout, dimension chunk c of a
-// tile is 1 KiB contiguous, so each float4 load of the wave is one coalesced
-// 1 KiB read.  The index query is uniform across the workgroup and is read
+// Mapping: one lane owns one group and a wavefront owns one pooled-key tile of
+// 64 groups; in the tiled layout, dimension chunk c of a tile is 1 KiB
+// contiguous, so each float4 load of the wave is one coalesced 1 KiB read.  The index query is uniform across the workgroup and is read
 // with scalar loads into SGPRs, so the fma operand costs no LDS or VALU work.
 // The workload is HBM-bound: 8 flop per pooled-key byte.
 #include "qsa_internal.h"
@@ -18,7 +17,15 @@
 namespace qsa {
 namespace {
 
-template <int HI, int DI, int TPW>
+// Pooled keys are read once per step, so they are loaded with the
+// nontemporal hint and do not displace the scores or other live data in L2.
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+template <int HI, int DI>
 __global__ void __launch_bounds__(kScoreWaves * kWave)
 score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled,
              const int64_t* __restrict__ pooled_off, const int32_t* __restrict__ seq_len,
@@ -30,93 +37,62 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
   if (!rv.valid) return;
   const int wave = (int)(threadIdx.x / kWave);
   const int lane = lane_id();
-  const int64_t tiles = (rv.g + 63) >> 6;
-  const int64_t t0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * TPW;
-  if (t0 >= tiles) return;
+  const int64_t tile = (int64_t)blockIdx.x * kScoreWaves + wave;  // 64 groups per wavefront
+  if (tile * 64 >= rv.g) return;
 
   const float* __restrict__ qrow = index_q + row * (int64_t)(HI * DI);
-  const float* __restrict__ kbase = pooled + pooled_off[rv.b] + t0 * (64 * DI) + lane * 4;
+  const float* __restrict__ kbase = pooled + pooled_off[rv.b] + tile * (64 * DI) + lane * 4;
 
-  bool tile_ok[TPW];
+  float acc[HI];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) tile_ok[i] = (t0 + i) < tiles;
+  for (int h = 0; h < HI; ++h) acc[h] = 0.0f;
 
-  float acc[TPW][HI];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i)
-#pragma unroll
-    for (int h = 0; h < HI; ++h) acc[i][h] = 0.0f;
-
-  // Register ring of PF dimension chunks per tile: the load of chunk c+PF is
-  // issued as soon as chunk c has been taken out of its slot, so PF x TPW
-  // KiB per wavefront stay in flight while the fma chains run.
+  // Register ring of PF dimension chunks: the load of chunk c+PF is issued as
+  // soon as chunk c leaves its slot.  A shallow ring keeps the register count
+  // low enough for 7-8 resident wavefronts per SIMD, which hides the memory
+  // latency better than a deeper ring at lower occupancy (measured).
   constexpr int NC = DI / 4;
-  constexpr int PF = NC < 4 ? NC : 4;
-  float4 ring[PF][TPW];
+  constexpr int PF = 2;
+  static_assert(NC % PF == 0, "ring depth must divide the chunk count");
+  float4 ring[PF];
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      ring[u][i] = tile_ok[i]
-                       ? *reinterpret_cast<const float4*>(kbase + (int64_t)i * (64 * DI) + u * 256)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int u = 0; u < PF; ++u) ring[u] = load_stream(kbase + u * 256);
 
 #pragma unroll 1
   for (int cb = 0; cb < NC; cb += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int c = cb + u;
-      float4 kv[TPW];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) kv[i] = ring[u][i];
-      if (c + PF < NC) {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-          if (tile_ok[i])
-            ring[u][i] = *reinterpret_cast<const float4*>(kbase + (int64_t)i * (64 * DI) +
-                                                          (c + PF) * 256);
-      }
+      const float4 kv = ring[u];
+      if (c + PF < NC) ring[u] = load_stream(kbase + (c + PF) * 256);
       const float* __restrict__ qc = qrow + 4 * c;
 #pragma unroll
       for (int h = 0; h < HI; ++h) {
-        const float q0 = qc[h * DI + 0];
-        const float q1 = qc[h * DI + 1];
-        const float q2 = qc[h * DI + 2];
-        const float q3 = qc[h * DI + 3];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          float a = acc[i][h];
-          a = __builtin_fmaf(q0, kv[i].x, a);
-          a = __builtin_fmaf(q1, kv[i].y, a);
-          a = __builtin_fmaf(q2, kv[i].z, a);
-          a = __builtin_fmaf(q3, kv[i].w, a);
-          acc[i][h] = a;
-        }
+        float a = acc[h];
+        a = __builtin_fmaf(qc[h * DI + 0], kv.x, a);
+        a = __builtin_fmaf(qc[h * DI + 1], kv.y, a);
+        a = __builtin_fmaf(qc[h * DI + 2], kv.z, a);
+        a = __builtin_fmaf(qc[h * DI + 3], kv.w, a);
+        acc[h] = a;
       }
     }
   }
 
-  float* __restrict__ srow = scores + lrow * g_max;
+  float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    if (!tile_ok[i]) break;
-    float s = 0.0f;
+  for (int h = 0; h < HI; ++h) s = s + (acc[h] > 0.0f ? acc[h] : 0.0f);
+  const int64_t g = tile * 64 + lane;
+  const bool ok = g < rv.g;
+  if (ok) scores[lrow * g_max + g] = s;
+  if (maxima) {
+    // maximum order key of the 16 consecutive groups sharing this DPP row
+    uint32_t m = ok ? order_key(s) : 0u;
 #pragma unroll
-    for (int h = 0; h < HI; ++h) s = s + (acc[i][h] > 0.0f ? acc[i][h] : 0.0f);
-    const int64_t g = (t0 + i) * 64 + lane;
-    const bool ok = g < rv.g;
-    if (ok) srow[g] = s;
-    if (maxima) {
-      // maximum order key of the 16 consecutive groups sharing this DPP row
-      uint32_t m = ok ? order_key(s) : 0u;
-#pragma unroll
-      for (int o = kSegment / 2; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)m, o, kWave);
-        m = m > y ? m : y;
-      }
-      if ((lane & (kSegment - 1)) == 0 && ok)
-        maxima[lrow * (g_max / kSegment) + g / kSegment] = m;
+    for (int o = kSegment / 2; o > 0; o >>= 1) {
+      const uint32_t y = (uint32_t)__shfl_xor((int)m, o, kWave);
+      m = m > y ? m : y;
     }
+    if ((lane & (kSegment - 1)) == 0 && ok) maxima[lrow * (g_max / kSegment) + g / kSegment] = m;
   }
 }
 
@@ -145,10 +121,9 @@ segment_maxima_kernel(const float* __restrict__ scores, const int32_t* __restric
 template <int HI, int DI>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int64_t tiles = (a.g_max + 63) / 64;
-  const int64_t per_block = (int64_t)kScoreWaves * kScoreTilesPerWave;
-  dim3 grid((unsigned)((tiles + per_block - 1) / per_block), (unsigned)a.rows);
+  dim3 grid((unsigned)((tiles + kScoreWaves - 1) / kScoreWaves), (unsigned)a.rows);
   if (grid.x == 0 || a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((score_kernel<HI, DI, kScoreTilesPerWave>), grid,
+  hipLaunchKernelGGL((score_kernel<HI, DI>), grid,
                      dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
                      a.seq_len, a.queries, a.g_max, a.row0, a.scores, a.maxima);
   return hipGetLastError();

@@ -30,12 +30,16 @@ namespace {
 constexpr int NT = kSelectThreads;
 constexpr int NWAVES = NT / kWave;
 
+constexpr int kMaxStage = 4096;   // segment maxima staged in LDS (G <= 65,536)
+constexpr int kPerThread = 32;    // scores held per thread in one streaming pass
+
 struct SelectShared {
   uint32_t hist[256];
   uint32_t wave_tot[NWAVES];
   uint32_t scal[4];
   uint32_t cand_key[kCandCap];
   uint32_t cand_pos[kCandCap];
+  uint32_t maxima[kMaxStage];
 };
 
 // Histogram add in which lanes of a wavefront that share a bin are first
@@ -180,44 +184,103 @@ select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ max
     kept = G;
   } else {
     const float* __restrict__ srow = scores + lrow * g_max;
-    // 1. threshold bound from the segment maxima
+    // 1. threshold bound from the segment maxima, staged once in LDS.  While
+    //    at least 2k would remain, f neighbouring maxima are folded into one
+    //    (their maximum): still one maximum per disjoint set of groups, so the
+    //    k-th largest of the folded values is still a lower bound of the k-th
+    //    largest score, and the radix select works on fewer values.
     uint32_t tau = 0;
     const uint32_t segs = (G + kSegment - 1) / kSegment;
     if (maxima && segs >= (uint32_t)k) {
+      const uint32_t* mrow = maxima + lrow * (g_max / kSegment);
+      uint32_t f = 1;
+      while (f < 8 && (segs / (2 * f)) >= 2u * (uint32_t)k) f *= 2;
+      const uint32_t nf = (segs + f - 1) / f;
       uint32_t above_unused;
-      radix_kth_largest(GlobalKeys{maxima + lrow * (g_max / kSegment)}, segs, (uint32_t)k, sh,
-                        &tau, &above_unused);
+      if (nf <= (uint32_t)kMaxStage) {
+        for (uint32_t i = tid; i < nf; i += NT) {
+          uint32_t m = 0;
+          for (uint32_t e = 0; e < f; ++e) {
+            const uint32_t j = i * f + e;
+            const uint32_t v = j < segs ? mrow[j] : 0u;
+            m = m > v ? m : v;
+          }
+          sh.maxima[i] = m;
+        }
+        __syncthreads();
+        radix_kth_largest(LdsCands{sh.maxima}, nf, (uint32_t)k, sh, &tau, &above_unused);
+      } else {
+        radix_kth_largest(GlobalKeys{mrow}, segs, (uint32_t)k, sh, &tau, &above_unused);
+      }
     }
-    // 2. ordered candidate compaction: 16 consecutive positions per thread
+    // 2. ordered candidate compaction.  A pass covers kPerThread*NT positions;
+    //    wavefront w owns a contiguous span of kPerThread*64 of them, read as
+    //    kPerThread/4 coalesced 1 KiB float4 loads (lane l holds positions
+    //    span + 256j + 4l .. +3).  Position order is (w, j, l, e), so a lane's
+    //    output index is the workgroup prefix of the wavefront totals, plus the
+    //    wavefront's running count over j, plus a bit-sliced ballot prefix over
+    //    the lanes below it.
     uint32_t n_cand = 0;
     bool overflow = false;
-    for (uint32_t base = 0; base < G; base += 16u * NT) {
-      const uint32_t p0 = base + 16u * tid;
-      uint32_t keys[16];
-      uint32_t flags = 0;
-      if (p0 + 16 <= G) {
+    constexpr int NJ = kPerThread / 4;
+    const int lane = lane_id();
+    const int wave = wave_id();
+    for (uint32_t base = 0; base < G; base += (uint32_t)kPerThread * NT) {
+      const uint32_t span = base + (uint32_t)wave * (kPerThread * kWave);
+      uint32_t keys[kPerThread];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4 f = *reinterpret_cast<const float4*>(srow + p0 + 4 * v);
-          keys[4 * v + 0] = order_key(f.x);
-          keys[4 * v + 1] = order_key(f.y);
-          keys[4 * v + 2] = order_key(f.z);
-          keys[4 * v + 3] = order_key(f.w);
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t p = span + 256u * j + 4u * lane;
+        if (p + 4 <= G) {
+          const float4 f4 = *reinterpret_cast<const float4*>(srow + p);
+          keys[4 * j + 0] = order_key(f4.x);
+          keys[4 * j + 1] = order_key(f4.y);
+          keys[4 * j + 2] = order_key(f4.z);
+          keys[4 * j + 3] = order_key(f4.w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keys[4 * j + e] = (p + e < G) ? order_key(srow[p + e]) : 0u;
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) keys[e] = (p0 + e < G) ? order_key(srow[p0 + e]) : 0u;
       }
+      uint32_t flags = 0;  // bit 4j+e: position span + 256j + 4*lane + e is a candidate
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (p0 + e < G && keys[e] >= tau) flags |= 1u << e;
-      uint32_t tot;
-      const uint32_t off = block_exclusive_sum<NT>((uint32_t)__popc(flags), sh.wave_tot, &tot);
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t p = span + 256u * j + 4u * lane + e;
+          if (p < G && keys[4 * j + e] >= tau) flags |= 1u << (4 * j + e);
+        }
+      // per j: this lane's count c (0..4) and the count over lanes below it
+      uint32_t below[NJ], wave_total = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t c = (uint32_t)__popc((flags >> (4 * j)) & 15u);
+        const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+        below[j] = wave_total + lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
+        wave_total += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+      }
+      if (lane == 0) sh.wave_tot[wave] = wave_total;
+      __syncthreads();
+      uint32_t wave_base = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NWAVES; ++w) {
+        const uint32_t t = sh.wave_tot[w];
+        wave_base += (w < wave) ? t : 0u;
+        tot += t;
+      }
+      __syncthreads();
       if (n_cand + tot > (uint32_t)kCandCap) { overflow = true; break; }
-      uint32_t o = n_cand + off;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((flags >> e) & 1u) { sh.cand_key[o] = keys[e]; sh.cand_pos[o] = p0 + e; ++o; }
+      for (int j = 0; j < NJ; ++j) {
+        uint32_t o = n_cand + wave_base + below[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((flags >> (4 * j + e)) & 1u) {
+            sh.cand_key[o] = keys[4 * j + e];
+            sh.cand_pos[o] = span + 256u * j + 4u * lane + e;
+            ++o;
+          }
+      }
       n_cand += tot;
     }
     __syncthreads();
