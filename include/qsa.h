@@ -158,6 +158,20 @@ QSA_API int qsa_score_groups(const qsa_shape *shape, const float *index_q, const
                      const int64_t *pooled_off, const int32_t *seq_len, float *scores,
                      qsa_stream stream);
 
+/* Step 1 for causal chunks (queries > 1), on MFMA: approx[r][g] is an
+ * approximation of the step-1 score of row r, group g, and bound[r][g] a
+ * certified bound on its distance to the exact (chained) score, derived from
+ * the standard floating-point summation error bounds and Cauchy-Schwarz.
+ * qsa_decode uses the same kernel for chunk rows and then rescores the
+ * groups the bounds cannot rule out with the exact chain, so its selection
+ * is identical to one decode per row (AFN-017 capsule evidence: chunk/decode
+ * equality).  Supported when index_heads is 4, 8 or 16 and queries is a
+ * multiple of 64/index_heads; QSA_ERR_UNSUPPORTED otherwise. */
+QSA_API int qsa_score_groups_chunk(const qsa_shape *shape, const float *index_q,
+                                   const float *pooled, const int64_t *pooled_off,
+                                   const int32_t *seq_len, float *approx, float *bound,
+                                   qsa_stream stream);
+
 /* Step 2: top-k membership per row by (score descending, group position
  * ascending); ties are resolved while choosing the set ([SET] §Decision and
  * §Tie handling belongs to membership).  Rows with G <= k keep every group.
@@ -209,7 +223,10 @@ QSA_API void qsa_timer_destroy(qsa_timer *timer);
 
 /* Steps 1-8 in one call: scores and per-16-group maxima, selection and
  * chronological emission (token_ids, width), resolve and compact gather,
- * online attention (out, lse).  Workspace >= qsa_workspace_bytes(shape)
+ * online attention (out, lse).  With queries > 1 and a shape that
+ * qsa_score_groups_chunk supports, step 1 runs on MFMA with certified bounds
+ * and the candidates are rescored exactly, so every row's result equals a
+ * decode of that row alone.  Workspace >= qsa_workspace_bytes(shape)
  * holds scores, maxima, compact K/V and attention partials.  timer may be
  * NULL.  Intermediate scratch contents are undefined after the call. */
 QSA_API int qsa_decode(const qsa_shape *shape, const float *index_q, const float *pooled,

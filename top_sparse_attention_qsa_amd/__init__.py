@@ -86,6 +86,7 @@ def lib():
             "qsa_workspace_bytes": ([S], sz),
             "qsa_pool_groups": ([S, P, P, P, P, P, P, P], ctypes.c_int),
             "qsa_score_groups": ([S, P, P, P, P, P, P], ctypes.c_int),
+            "qsa_score_groups_chunk": ([S, P, P, P, P, P, P, P], ctypes.c_int),
             "qsa_select_topk": ([S, P, P, P, P, sz, P], ctypes.c_int),
             "qsa_emit_chronological": ([S, P, P, P, P, P], ctypes.c_int),
             "qsa_resolve_gather": ([S, P, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
@@ -161,6 +162,15 @@ def qsa_score_groups(shape, index_q, pooled, pooled_off, seq_len, scores, stream
         _ptr(pooled, torch.float32, "pooled"), _ptr(pooled_off, torch.int64, "pooled_off"),
         _ptr(seq_len, torch.int32, "seq_len"), _ptr(scores, torch.float32, "scores"),
         _stream(stream)), "qsa_score_groups")
+
+
+def qsa_score_groups_chunk(shape, index_q, pooled, pooled_off, seq_len, approx, bound,
+                           stream=None):
+    _check(lib().qsa_score_groups_chunk(
+        ctypes.byref(shape), _ptr(index_q, torch.float32, "index_q"),
+        _ptr(pooled, torch.float32, "pooled"), _ptr(pooled_off, torch.int64, "pooled_off"),
+        _ptr(seq_len, torch.int32, "seq_len"), _ptr(approx, torch.float32, "approx"),
+        _ptr(bound, torch.float32, "bound"), _stream(stream)), "qsa_score_groups_chunk")
 
 
 def qsa_select_topk(shape, scores, seq_len, sel_bitmap, workspace, stream=None):

@@ -164,6 +164,19 @@ int qsa_score_groups(const qsa_shape* s, const float* index_q, const float* pool
   return hip_status(launch_score(a, s->index_heads, s->index_dim, (hipStream_t)stream));
 }
 
+int qsa_score_groups_chunk(const qsa_shape* s, const float* index_q, const float* pooled,
+                           const int64_t* pooled_off, const int32_t* seq_len, float* approx,
+                           float* bound, qsa_stream stream) {
+  int rc = validate(s, kNeedIndex);
+  if (rc != QSA_OK) return rc;
+  if (!index_q || !pooled || !pooled_off || !seq_len || !approx || !bound) return QSA_ERR_NULL;
+  if (!aligned16(pooled)) return QSA_ERR_SHAPE;
+  if (!chunk_supported(s->index_heads, s->queries, row_count(s))) return QSA_ERR_UNSUPPORTED;
+  ChunkArgs a{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, 0, row_count(s),
+              approx, bound, nullptr, nullptr};
+  return hip_status(launch_chunk(a, s->index_heads, s->index_dim, (hipStream_t)stream));
+}
+
 int qsa_select_topk(const qsa_shape* s, const float* scores, const int32_t* seq_len,
                     uint32_t* sel_bitmap, void* ws, size_t ws_bytes, qsa_stream stream) {
   int rc = validate(s, kNeedBudget | kNeedAttn);
@@ -323,18 +336,32 @@ int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
   hipStream_t st = (hipStream_t)stream;
   hipEvent_t* ev = timer ? timer->ev + (size_t)timer->calls * (QSA_DECODE_STAGES + 1) : nullptr;
   const int64_t rows = row_count(s), R = rows_per_pass(s);
+  // causal chunks score on MFMA with certified bounds and an exact rescoring
+  // of the candidates; decode rows (or unsupported chunk shapes) use the chain
+  const bool chunk = s->queries > 1 && chunk_supported(s->index_heads, s->queries, R);
 
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
     const int64_t n = (rows - r0) < R ? (rows - r0) : R;
     const bool timed = ev && r0 == 0;  // with several passes the events bracket the first
     if (timed && hipEventRecord(ev[0], st) != hipSuccess) return QSA_ERR_HIP;
-    ScoreArgs sa{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
-                 scores, maxima};
-    if (launch_score(sa, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
+    if (chunk) {
+      ChunkArgs ca{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
+                   nullptr, nullptr, scores, maxima};
+      if (launch_chunk(ca, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
+    } else {
+      ScoreArgs sa{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
+                   scores, maxima};
+      if (launch_score(sa, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
+    }
     if (timed && hipEventRecord(ev[1], st) != hipSuccess) return QSA_ERR_HIP;
     SelectArgs se{scores, maxima, seq_len, s->queries, s->max_groups, s->budget_groups,
                   r0, n, nullptr, token_ids, width};
-    if (launch_select(se, st) != hipSuccess) return QSA_ERR_HIP;
+    if (chunk) {
+      RescoreArgs ra{index_q, pooled, pooled_off, s->index_heads, s->index_dim};
+      if (launch_select_certified(se, ra, st) != hipSuccess) return QSA_ERR_HIP;
+    } else if (launch_select(se, st) != hipSuccess) {
+      return QSA_ERR_HIP;
+    }
     if (timed && hipEventRecord(ev[2], st) != hipSuccess) return QSA_ERR_HIP;
     GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
                   s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, r0, n, kc, vc,

@@ -174,6 +174,30 @@ struct AttendArgs {
   float* lse;                // global rows, may be null
 };
 
+struct ChunkArgs {
+  const float* index_q;      // global rows
+  const float* pooled;
+  const int64_t* pooled_off;
+  const int32_t* seq_len;
+  int32_t queries;
+  int64_t g_max;
+  int64_t row0;
+  int64_t rows;              // a multiple of 4*16/H_I
+  float* approx;             // [rows][g_max] approximate scores, may be null
+  float* bound;              // [rows][g_max] certified error bounds, may be null
+  float* hi;                 // [rows][g_max] approx + bound, may be null
+  uint32_t* lo_maxima;       // [rows][g_max/16] order keys of approx - bound, may be null
+};
+
+// Exact rescoring inputs for the certified selection (chunk rows).
+struct RescoreArgs {
+  const float* index_q;      // global rows
+  const float* pooled;
+  const int64_t* pooled_off;
+  int32_t index_heads;
+  int32_t index_dim;
+};
+
 struct PoolArgs {
   const float* raw_keys;
   const int64_t* raw_off;
@@ -198,5 +222,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+bool chunk_supported(int h_i, int queries, int64_t rows_per_launch);
+hipError_t launch_chunk(const ChunkArgs& a, int h_i, int d_i, hipStream_t s);
+hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hipStream_t s);
 
 }  // namespace qsa

@@ -133,6 +133,55 @@ struct LdsCands {
   __device__ uint32_t key(uint32_t i) const { return k[i]; }
 };
 
+// Policy of the plain (decode) selection: the row's scores are exact.
+struct PlainScores {
+  static constexpr bool kCertified = false;
+  const float* srow;
+  __device__ uint32_t full_key(uint32_t g) const { return order_key(srow[g]); }
+  __device__ uint32_t exact_key(uint32_t g) const { return order_key(srow[g]); }
+};
+
+// Policy of the certified (chunk) selection: the row's "scores" are upper
+// bounds hi = s~ + E of the chain scores (chunk.hip), so candidates are
+// rescored here with the chain itself -- the same fused multiply-adds, in the
+// same order, as score.hip -- before the exact selection.
+template <int HI, int DI>
+struct CertifiedScores {
+  static constexpr bool kCertified = true;
+  const float* q;    // this row's index query [HI][DI]
+  const float* kp;   // this sequence's tiled pooled keys
+  __device__ uint32_t exact_key(uint32_t g) const {
+    const float* kb = kp + (int64_t)(g >> 6) * (64 * DI) + (g & 63) * 4;
+    float acc[HI];
+#pragma unroll
+    for (int h = 0; h < HI; ++h) acc[h] = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < DI / 4; ++c) {
+      const float4 kv = *reinterpret_cast<const float4*>(kb + c * 256);
+#pragma unroll
+      for (int h = 0; h < HI; ++h) {
+        float a = acc[h];
+        a = __builtin_fmaf(q[h * DI + 4 * c + 0], kv.x, a);
+        a = __builtin_fmaf(q[h * DI + 4 * c + 1], kv.y, a);
+        a = __builtin_fmaf(q[h * DI + 4 * c + 2], kv.z, a);
+        a = __builtin_fmaf(q[h * DI + 4 * c + 3], kv.w, a);
+        acc[h] = a;
+      }
+    }
+    float sc = 0.0f;
+#pragma unroll
+    for (int h = 0; h < HI; ++h) sc = sc + (acc[h] > 0.0f ? acc[h] : 0.0f);
+    return order_key(sc);
+  }
+  __device__ uint32_t full_key(uint32_t g) const { return exact_key(g); }
+};
+
+template <class P>
+struct FullKeys {
+  const P* pol;
+  __device__ uint32_t key(uint32_t i) const { return pol->full_key(i); }
+};
+
 // Writes kept group g at output index o: token IDs 4g..4g+3 at 4o, and/or
 // bit g of the bitmap.
 struct Emitter {
@@ -148,16 +197,12 @@ struct Emitter {
   }
 };
 
-__global__ void __launch_bounds__(NT)
-select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ maxima,
-              const int32_t* __restrict__ seq_len, int32_t queries, int64_t g_max, int32_t k,
-              int64_t row0, uint32_t* __restrict__ bitmap, int32_t* __restrict__ token_ids,
-              int32_t* __restrict__ width) {
-  __shared__ SelectShared sh;
+template <class P>
+__device__ void select_row(const P& pol, SelectShared& sh, const float* __restrict__ scores,
+                           const uint32_t* __restrict__ maxima, const RowView& rv, int64_t lrow,
+                           int64_t row, int64_t g_max, int32_t k, uint32_t* __restrict__ bitmap,
+                           int32_t* __restrict__ token_ids, int32_t* __restrict__ width) {
   const int tid = (int)threadIdx.x;
-  const int64_t lrow = blockIdx.x;
-  const int64_t row = row0 + lrow;
-  const RowView rv = row_view(seq_len, row, queries, g_max);
   const int32_t stride = 4 * k + 4;
   int32_t* ids = token_ids ? token_ids + row * stride : nullptr;
   uint32_t* bm = bitmap ? bitmap + row * (g_max / 32) : nullptr;
@@ -284,12 +329,21 @@ select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ max
       n_cand += tot;
     }
     __syncthreads();
+    if constexpr (P::kCertified) {
+      // the candidates' bounds are replaced by their exact (chain) keys
+      if (!overflow) {
+        for (uint32_t i = tid; i < n_cand; i += NT) sh.cand_key[i] = pol.exact_key(sh.cand_pos[i]);
+        __syncthreads();
+      }
+    }
 
-    // 3. exact k-th largest key and the count above it
+    // 3. exact k-th largest key and the count above it (with too many
+    //    candidates, the keys of the whole row are streamed -- computed exactly
+    //    on the fly for certified rows)
     uint32_t T, above;
     const uint32_t n_src = overflow ? G : n_cand;
     if (overflow)
-      radix_kth_largest(GlobalScores{srow}, G, (uint32_t)k, sh, &T, &above);
+      radix_kth_largest(FullKeys<P>{&pol}, G, (uint32_t)k, sh, &T, &above);
     else
       radix_kth_largest(LdsCands{sh.cand_key}, n_cand, (uint32_t)k, sh, &T, &above);
     const uint32_t need = (uint32_t)k - above;  // keys equal to T to keep, lowest positions first
@@ -303,7 +357,7 @@ select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ max
       for (int e = 0; e < 4; ++e) {
         const uint32_t i = i0 + e;
         if (i < n_src) {
-          key[e] = overflow ? order_key(srow[i]) : sh.cand_key[i];
+          key[e] = overflow ? pol.full_key(i) : sh.cand_key[i];
           pos[e] = overflow ? i : sh.cand_pos[i];
         } else {
           key[e] = 0u;
@@ -348,6 +402,36 @@ select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ max
       ids[i] = (i < w) ? (int32_t)(4 * rv.g + (i - body)) : -1;
   }
   if (width && tid == 0) width[row] = 4 * (int32_t)kept + rv.tail;
+}
+
+__global__ void __launch_bounds__(NT)
+select_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ maxima,
+              const int32_t* __restrict__ seq_len, int32_t queries, int64_t g_max, int32_t k,
+              int64_t row0, uint32_t* __restrict__ bitmap, int32_t* __restrict__ token_ids,
+              int32_t* __restrict__ width) {
+  __shared__ SelectShared sh;
+  const int64_t lrow = blockIdx.x;
+  const int64_t row = row0 + lrow;
+  const RowView rv = row_view(seq_len, row, queries, g_max);
+  const PlainScores pol{scores + lrow * g_max};
+  select_row(pol, sh, scores, maxima, rv, lrow, row, g_max, k, bitmap, token_ids, width);
+}
+
+template <int HI, int DI>
+__global__ void __launch_bounds__(NT)
+select_certified_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ maxima,
+                        const int32_t* __restrict__ seq_len, int32_t queries, int64_t g_max,
+                        int32_t k, int64_t row0, uint32_t* __restrict__ bitmap,
+                        int32_t* __restrict__ token_ids, int32_t* __restrict__ width,
+                        const float* __restrict__ index_q, const float* __restrict__ pooled,
+                        const int64_t* __restrict__ pooled_off) {
+  __shared__ SelectShared sh;
+  const int64_t lrow = blockIdx.x;
+  const int64_t row = row0 + lrow;
+  const RowView rv = row_view(seq_len, row, queries, g_max);
+  const CertifiedScores<HI, DI> pol{index_q + row * (int64_t)(HI * DI),
+                                    pooled + (rv.valid ? pooled_off[rv.b] : 0)};
+  select_row(pol, sh, scores, maxima, rv, lrow, row, g_max, k, bitmap, token_ids, width);
 }
 
 // Bitmap -> chronological token IDs: popcount prefix over the words in order.
@@ -421,6 +505,34 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
                      a.seq_len, a.queries, a.g_max, a.k, a.row0, a.bitmap, a.token_ids,
                      a.width);
   return hipGetLastError();
+}
+
+template <int HI, int DI>
+hipError_t launch_cert_t(const SelectArgs& a, const RescoreArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL((select_certified_kernel<HI, DI>), dim3((unsigned)a.rows), dim3(NT), 0, s,
+                     a.scores, a.maxima, a.seq_len, a.queries, a.g_max, a.k, a.row0, a.bitmap,
+                     a.token_ids, a.width, r.index_q, r.pooled, r.pooled_off);
+  return hipGetLastError();
+}
+
+template <int HI>
+hipError_t launch_cert_h(const SelectArgs& a, const RescoreArgs& r, hipStream_t s) {
+  switch (r.index_dim) {
+    case 32: return launch_cert_t<HI, 32>(a, r, s);
+    case 64: return launch_cert_t<HI, 64>(a, r, s);
+    case 128: return launch_cert_t<HI, 128>(a, r, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  switch (r.index_heads) {
+    case 4: return launch_cert_h<4>(a, r, s);
+    case 8: return launch_cert_h<8>(a, r, s);
+    case 16: return launch_cert_h<16>(a, r, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_emit(const uint32_t* bitmap, const int32_t* seq_len, int32_t queries,
