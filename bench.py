@@ -45,6 +45,19 @@ def algorithmic_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=128, k=5
                 attend_merge=merge)
 
 
+def fused_algorithmic_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=128, k=512):
+    """The same step with resolve+gather inside the attention: IDs and slot-map
+    entries are read once and the selected K/V rows once, straight from the
+    cache; no compact scratch is written or re-read."""
+    a = algorithmic_bytes(B, G, h_i, d_i, h_q, h_kv, d, k)
+    W = 4 * k
+    kv_row = h_kv * d * 4
+    chunks = math.ceil((4 * k + 3) / 64)
+    fused_attend = (B * W * 4 * 2 + 2 * B * W * kv_row + B * h_q * d * 4
+                    + B * h_q * chunks * (d + 2) * 4)
+    return a["score"] + a["select_emit"] + fused_attend + a["attend_merge"]
+
+
 def source_digest():
     h = hashlib.sha256()
     for f in ("score.hip", "qsa_internal.h"):
@@ -187,6 +200,25 @@ def main():
     stage_ms = {name: sum(c[i] for c in stage) / len(stage)
                 for i, name in enumerate(qsa.STAGE_NAMES)}
 
+    # the same step with the gather fused into the attention (no compact scratch)
+    print(f"[bench] timing {args.steps} fused steps", file=sys.stderr, flush=True)
+    ref_out = case.out.clone()
+    for _ in range(args.warmup):
+        case.decode(fused=True)
+    ftimer = qsa.Timer(args.steps)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        case.decode(ftimer, fused=True)
+    stop.record()
+    torch.cuda.synchronize()
+    fused_ms = start.elapsed_time(stop) / args.steps
+    fstage = ftimer.read()
+    ftimer.close()
+    fused_stage_ms = {name: sum(c[i] for c in fstage) / len(fstage)
+                      for i, name in enumerate(qsa.STAGE_NAMES)}
+    assert torch.equal(case.out, ref_out), "fused path differs from the compact path"
+
     alg = algorithmic_bytes()
     step_bytes = sum(alg.values())
     score_ms = stage_ms["score"]
@@ -230,6 +262,15 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg["score"],
             "mean_launch_ms": score_ms,
+        },
+        "fused": {
+            "note": "same step with resolve+gather fused into the attention kernel "
+                    "(no compact scratch); bit-identical outputs",
+            "value": rows / (fused_ms * 1e-3),
+            "ms_per_step": fused_ms,
+            "algorithmic_bytes": fused_algorithmic_bytes(),
+            "hbm_gbps": fused_algorithmic_bytes() / (fused_ms * 1e-3) / 1e9,
+            "stage_ms": fused_stage_ms,
         },
         "cpu_baseline": None,
     }

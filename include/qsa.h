@@ -236,6 +236,21 @@ QSA_API int qsa_decode(const qsa_shape *shape, const float *index_q, const float
                float *out, float *lse, void *workspace, size_t workspace_bytes,
                qsa_timer *timer, qsa_stream stream);
 
+/* Steps 1-8 with steps 6-8 fused: the attention kernel resolves each
+ * selected logical ID once through the slot map and reads the K/V rows
+ * straight from the cache, so no compact scratch is written or read
+ * ([MASK] §Why compact gather comes before fusion: a later fused
+ * indirect-load kernel may replace the gather, keeping the logical-ID
+ * contract and the zero dense-mask allocation).  Same arguments, workspace
+ * and results as qsa_decode, bit for bit; the timer's gather stage is empty. */
+QSA_API int qsa_decode_fused(const qsa_shape *shape, const float *index_q, const float *pooled,
+                             const int64_t *pooled_off, const int32_t *seq_len,
+                             const int32_t *slot_map, const int64_t *slot_off,
+                             const float *k_cache, const float *v_cache, const float *q,
+                             float softmax_scale, int32_t *token_ids, int32_t *width, float *out,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             qsa_timer *timer, qsa_stream stream);
+
 /* Host-only byte ledger for a cache of total_tokens tokens ([MASK] §What
  * the checkpoint measures; the dense-mask count is always 0). */
 QSA_API int qsa_accounting(const qsa_shape *shape, int64_t total_tokens, qsa_bytes *out_host);

@@ -54,11 +54,11 @@ class GpuCase:
         self.out = torch.empty((rows, s.h_q, s.d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((rows, s.h_q), dtype=torch.float32, device=dev)
 
-    def decode(self, timer=None):
+    def decode(self, timer=None, fused=False):
         qsa.qsa_decode(self.shape, self.index_q, self.pooled, self.pooled_off, self.seq_len,
                        self.slot_map, self.slot_off, self.k_cache, self.v_cache, self.q,
                        self.scale, self.token_ids, self.width, self.out, self.lse,
-                       self.workspace, timer)
+                       self.workspace, timer, fused=fused)
 
 
 def host(t):

@@ -60,3 +60,11 @@ def test_c4_repeat_is_bitwise_identical(c4):
     torch.cuda.synchronize()
     assert torch.equal(ref[0], c4.token_ids)
     assert torch.equal(ref[1], c4.out) and torch.equal(ref[2], c4.lse)
+
+
+def test_c4_fused_equals_compact(c4):
+    ref = (c4.token_ids.clone(), c4.width.clone(), c4.out.clone(), c4.lse.clone())
+    c4.decode(fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], c4.token_ids) and torch.equal(ref[1], c4.width)
+    assert torch.equal(ref[2], c4.out) and torch.equal(ref[3], c4.lse)

@@ -298,3 +298,57 @@ def test_out_of_range_slots_give_nan_rows():
                            case.slot_off, case.k_cache, case.v_cache, kc, vc, phys)
     assert int(phys[0, 5]) == -1 and torch.isnan(kc[0, 5]).all()
     assert torch.isnan(case.out[0]).all()
+
+
+# ---------------------------------------------------------- fused gather
+
+def _fused_copy(case):
+    fused = harness.GpuCase(case.data, rows_in_flight=case.shape.rows_in_flight)
+    fused.decode(fused=True)
+    torch.cuda.synchronize()
+    return fused
+
+
+def test_fused_equals_compact(named):
+    """Fusing the gather into the attention reads the same rows in the same
+    order: identical bits (AFN-016 §Why compact gather comes before fusion)."""
+    fused = _fused_copy(named)
+    assert torch.equal(fused.token_ids, named.token_ids)
+    assert torch.equal(fused.width, named.width)
+    assert torch.equal(fused.out, named.out) and torch.equal(fused.lse, named.lse)
+
+
+@pytest.mark.parametrize("h_i,d_i,h_q,h_kv,d", [(1, 32, 2, 2, 64), (4, 128, 16, 1, 64),
+                                                (16, 32, 16, 16, 128)])
+def test_fused_ragged_shapes(h_i, d_i, h_q, h_kv, d):
+    lens = [0, 3, 63, 64, 65, 257, 1000, 4097]
+    spec = inputs.custom("ragged_f", lens, h_i=h_i, d_i=d_i, h_q=h_q, h_kv=h_kv, d=d, budget=16,
+                         keys="grid", slots="perm")
+    data = inputs.make(spec, seed=h_i * 5 + d, device="cpu")
+    case = harness.GpuCase(data)
+    case.decode()
+    fused = _fused_copy(case)
+    assert torch.equal(fused.token_ids, case.token_ids)
+    assert torch.equal(fused.out, case.out) and torch.equal(fused.lse, case.lse)
+
+
+def test_fused_out_of_range_slot_gives_nan():
+    spec = inputs.custom("slots_f", [300, 700], h_i=4, d_i=32, h_q=2, h_kv=1, d=64)
+    data = inputs.make(spec, seed=3, device="cpu")
+    case = harness.GpuCase(data)
+    case.slot_map[5] = case.shape.kv_slots + 3
+    case.decode(fused=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(case.out[0]).all()
+    check_rows(case, rows=[1])
+
+
+def test_fused_chunk_rows_equal_compact():
+    spec = inputs.custom("chunk_f", [2100, 9000], queries=16, h_i=16, d_i=64, h_q=8, h_kv=2,
+                         d=128, budget=512, keys="normal", slots="perm")
+    data = inputs.make(spec, seed=12, device="cpu")
+    case = harness.GpuCase(data)
+    case.decode()
+    fused = _fused_copy(case)
+    assert torch.equal(fused.token_ids, case.token_ids)
+    assert torch.equal(fused.out, case.out) and torch.equal(fused.lse, case.lse)

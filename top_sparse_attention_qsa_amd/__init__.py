@@ -97,6 +97,8 @@ def lib():
             "qsa_timer_destroy": ([P], None),
             "qsa_decode": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
                            ctypes.c_int),
+            "qsa_decode_fused": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
+                                 ctypes.c_int),
             "qsa_accounting": ([S, i64, ctypes.POINTER(Bytes)], ctypes.c_int),
             "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "qsa_version": ([], ctypes.c_char_p),
@@ -213,8 +215,9 @@ def qsa_online_attend(shape, q, k_compact, v_compact, width, softmax_scale, out,
 
 def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
                v_cache, q, softmax_scale, token_ids, width, out, lse, workspace, timer=None,
-               stream=None):
-    _check(lib().qsa_decode(
+               stream=None, fused=False):
+    fn = lib().qsa_decode_fused if fused else lib().qsa_decode
+    _check(fn(
         ctypes.byref(shape), _ptr(index_q, torch.float32, "index_q"),
         _ptr(pooled, torch.float32, "pooled"), _ptr(pooled_off, torch.int64, "pooled_off"),
         _ptr(seq_len, torch.int32, "seq_len"), _ptr(slot_map, torch.int32, "slot_map"),
@@ -224,7 +227,12 @@ def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, 
         _ptr(width, torch.int32, "width"), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse", True), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), timer.handle if timer is not None else None, _stream(stream)),
-        "qsa_decode")
+        "qsa_decode_fused" if fused else "qsa_decode")
+
+
+def qsa_decode_fused(*args, **kw):
+    """qsa_decode with the gather fused into the attention (no compact scratch)."""
+    return qsa_decode(*args, fused=True, **kw)
 
 
 def qsa_accounting(shape, total_tokens):

@@ -308,7 +308,9 @@ void qsa_timer_destroy(qsa_timer* t) {
   delete t;
 }
 
-int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
+}  // extern "C"
+
+static int decode_impl(bool fused, const qsa_shape* s, const float* index_q, const float* pooled,
                const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
                const int64_t* slot_off, const float* k_cache, const float* v_cache,
                const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
@@ -363,13 +365,25 @@ int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
       return QSA_ERR_HIP;
     }
     if (timed && hipEventRecord(ev[2], st) != hipSuccess) return QSA_ERR_HIP;
-    GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
-                  s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, r0, n, kc, vc,
-                  nullptr};
-    if (launch_gather(ga, st) != hipSuccess) return QSA_ERR_HIP;
+    if (!fused) {
+      GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
+                    s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, r0, n, kc, vc,
+                    nullptr};
+      if (launch_gather(ga, st) != hipSuccess) return QSA_ERR_HIP;
+    }
     if (timed && hipEventRecord(ev[3], st) != hipSuccess) return QSA_ERR_HIP;
     AttendArgs aa{q, kc, vc, width, s->q_heads, s->kv_heads, s->head_dim, token_stride(s),
                   attn_chunks(s), softmax_scale, r0, n, pacc, pml, out, lse};
+    if (fused) {
+      aa.token_ids = token_ids;
+      aa.seq_len = seq_len;
+      aa.slot_map = slot_map;
+      aa.slot_off = slot_off;
+      aa.k_cache = k_cache;
+      aa.v_cache = v_cache;
+      aa.kv_slots = s->kv_slots;
+      aa.queries = s->queries;
+    }
     if (launch_attend(aa, st) != hipSuccess) return QSA_ERR_HIP;
     if (timed && hipEventRecord(ev[4], st) != hipSuccess) return QSA_ERR_HIP;
     if (launch_merge(aa, st) != hipSuccess) return QSA_ERR_HIP;
@@ -377,6 +391,31 @@ int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
   }
   if (timer) timer->calls += 1;
   return QSA_OK;
+}
+
+
+extern "C" {
+
+int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
+               const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
+               const int64_t* slot_off, const float* k_cache, const float* v_cache,
+               const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
+               float* out, float* lse, void* ws, size_t ws_bytes, qsa_timer* timer,
+               qsa_stream stream) {
+  return decode_impl(false, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
+                     v_cache, q, softmax_scale, token_ids, width, out, lse, ws, ws_bytes, timer,
+                     stream);
+}
+
+int qsa_decode_fused(const qsa_shape* s, const float* index_q, const float* pooled,
+                     const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
+                     const int64_t* slot_off, const float* k_cache, const float* v_cache,
+                     const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
+                     float* out, float* lse, void* ws, size_t ws_bytes, qsa_timer* timer,
+                     qsa_stream stream) {
+  return decode_impl(true, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
+                     v_cache, q, softmax_scale, token_ids, width, out, lse, ws, ws_bytes, timer,
+                     stream);
 }
 
 }  // extern "C"

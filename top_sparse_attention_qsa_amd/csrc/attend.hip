@@ -30,9 +30,9 @@ constexpr int C = kAttnChunk;
 
 template <int D, int GQ>
 struct AttnCfg {
-  static constexpr int NW = GQ < 4 ? GQ : 4;
+  static constexpr int NW = 4;           // wavefronts; with GQ < 4 some have no score work
   static constexpr int NT = NW * kWave;
-  static constexpr int HPW = GQ / NW;    // query heads per wavefront in the score phase
+  static constexpr int HPW = (GQ + NW - 1) / NW;  // query heads per wavefront (score phase)
   static constexpr int KPW = C / NW;     // compact rows per wavefront in the P.V phase
   static constexpr int KP = D + 4;       // padded K row, floats
   static constexpr int DPL = D / kWave;  // output dims per lane
@@ -60,10 +60,29 @@ __device__ __forceinline__ Item item_of(int64_t it, int64_t rows, int kv_heads) 
   return x;
 }
 
-template <int D, int GQ>
-__global__ void __launch_bounds__((GQ < 4 ? GQ : 4) * kWave)
-attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_compact,
-                    const float* __restrict__ v_compact, const int32_t* __restrict__ width,
+// Where a work item's K and V rows come from.  Compact: the scratch written
+// by the gather (row i of the row's compact copy).  Fused: straight from the
+// K/V cache; the chunk's logical IDs are resolved through the slot map once,
+// inside this kernel, two items ahead of their use, into a three-deep LDS
+// ring (wavefront 0: ID loads at the top of an item, slot-map loads after its
+// scores, LDS write at its end), so the row loads of the next item can be
+// issued as early as in the compact path.  Both produce the same bits.
+struct RowSource {
+  const float* k_compact;
+  const float* v_compact;
+  const int32_t* token_ids;  // fused only, global rows
+  const int32_t* seq_len;
+  const int32_t* slot_map;
+  const int64_t* slot_off;
+  const float* k_cache;
+  const float* v_cache;
+  int64_t kv_slots;
+  int32_t queries;
+};
+
+template <int D, int GQ, bool FUSED>
+__global__ void __launch_bounds__(4 * kWave)
+attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* __restrict__ width,
                     int32_t q_heads, int32_t kv_heads, int32_t stride, int32_t n_chunks,
                     float scale, int64_t row0, int64_t rows, float* __restrict__ part_acc,
                     float* __restrict__ part_ml) {
@@ -72,6 +91,7 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
   constexpr int DPL = A::DPL, KV4 = A::KV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
   __shared__ float4 ps4[GQ * C / 4];
+  __shared__ int32_t ring[FUSED ? 3 : 1][C];  // resolved slots (-1: invalid ID or slot)
   float* smem = reinterpret_cast<float*>(smem4);
   float* ps = reinterpret_cast<float*>(ps4);
 
@@ -79,7 +99,7 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
   const int wave = wave_id();
   const int lane = lane_id();
   const int64_t items = (int64_t)n_chunks * rows * kv_heads;
-  const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact rows
+  const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact or cache rows
 
   // Every load is unconditional: rows past a chunk's width read the chunk's
   // last valid row (always in bounds); their K rows are zeroed in LDS and
@@ -92,74 +112,142 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
     if (w <= 0 || w > stride - 1 || c0 >= w) return 0;
     return (w - c0) < C ? (w - c0) : C;
   };
-  auto base_of = [&](const float* base, const Item& x) -> const float* {
-    return base + ((x.lrow * stride + (int64_t)x.chunk * C) * kv_heads + x.hk) * (int64_t)D;
+  // address of row i (< cn) of item x for KV head x.hk, in K or V
+  auto row_ptr = [&](const float* compact, const float* cache, const Item& x, int i,
+                     int ring_slot) -> const float* {
+    if constexpr (FUSED) {
+      const int32_t sl = ring[ring_slot][i];
+      return cache + (int64_t)(sl >= 0 ? sl : 0) * rstride + (int64_t)x.hk * D;
+    } else {
+      return compact + ((x.lrow * stride + (int64_t)x.chunk * C + i) * kv_heads + x.hk) *
+                           (int64_t)D;
+    }
   };
   float4 kst[KV4];
   float vreg[KPW][DPL];
-  auto load_k = [&](const Item& x, int cn_raw) {
+  auto load_k = [&](const Item& x, int cn_raw, int ring_slot) {
     const int cn = cn_raw > 0 ? cn_raw : 1;
-    const float* kb = base_of(k_compact, x);
 #pragma unroll
     for (int r = 0; r < KV4; ++r) {
       const int e = tid + r * NT;
       const int i = e / (D / 4);
       const int c = e - i * (D / 4);
       const int ic = i < cn ? i : cn - 1;
-      kst[r] = *reinterpret_cast<const float4*>(kb + ic * rstride + 4 * c);
+      kst[r] = *reinterpret_cast<const float4*>(
+          row_ptr(src.k_compact, src.k_cache, x, ic, ring_slot) + 4 * c);
     }
   };
-  auto load_v = [&](const Item& x, int cn_raw) {
+  auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
     const int cn = cn_raw > 0 ? cn_raw : 1;
-    const float* vb = base_of(v_compact, x);
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       const int i = wave * KPW + j;
       const int ic = i < cn ? i : cn - 1;
+      const float* vp = row_ptr(src.v_compact, src.v_cache, x, ic, ring_slot);
       if constexpr (DPL == 2) {
-        const float2 v2 = *reinterpret_cast<const float2*>(vb + ic * rstride + 2 * lane);
+        const float2 v2 = *reinterpret_cast<const float2*>(vp + 2 * lane);
         vreg[j][0] = v2.x;
         vreg[j][1] = v2.y;
       } else {
-        vreg[j][0] = vb[ic * rstride + lane];
+        vreg[j][0] = vp[lane];
       }
+    }
+  };
+  // Fused resolution of item x in three phases on wavefront 0, lane i = row i.
+  int32_t id_reg = -1, slot_reg = 0;
+  auto resolve_ids = [&](const Item& x, int cn_x) {
+    if constexpr (FUSED) {
+      if (wave == 0) {
+        const int64_t row = row0 + x.lrow;
+        id_reg = lane < cn_x ? src.token_ids[row * stride + (int64_t)x.chunk * C + lane] : -1;
+      }
+    }
+  };
+  auto resolve_slots = [&](const Item& x, int cn_x) {
+    if constexpr (FUSED) {
+      if (wave == 0) {
+        const int64_t row = row0 + x.lrow;
+        const int32_t b = (int32_t)(row / src.queries);
+        const int64_t n = (int64_t)src.seq_len[b] - src.queries + 1 + (row - (int64_t)b * src.queries);
+        slot_reg = lane < cn_x ? -1 : 0;
+        if (lane < cn_x && id_reg >= 0 && (int64_t)id_reg < n) {
+          const int32_t sl = src.slot_map[src.slot_off[b] + id_reg];
+          slot_reg = (sl >= 0 && (int64_t)sl < src.kv_slots) ? sl : -1;
+        }
+      }
+    }
+  };
+  auto resolve_store = [&](int ring_slot) {
+    if constexpr (FUSED) {
+      if (wave == 0) ring[ring_slot][lane] = slot_reg;
     }
   };
 
   int64_t it = blockIdx.x;
-  Item cur = item_of(it < items ? it : items - 1, rows, kv_heads);
-  int cn = it < items ? chunk_rows(cur) : 0;
-  load_k(cur, cn);
-  load_v(cur, cn);
+  int j = 0;  // this workgroup's item sequence number
+  auto item_at = [&](int64_t i) { return item_of(i < items ? i : items - 1, rows, kv_heads); };
+  auto rows_at = [&](int64_t i, const Item& x) { return i < items ? chunk_rows(x) : 0; };
+  Item cur = item_at(it);
+  int cn = rows_at(it, cur);
+  if constexpr (FUSED) {
+    // items 0 and 1 of this workgroup are resolved up front
+    const Item x1 = item_at(it + gridDim.x);
+    resolve_ids(cur, cn);
+    resolve_slots(cur, cn);
+    resolve_store(0);
+    resolve_ids(x1, rows_at(it + gridDim.x, x1));
+    resolve_slots(x1, rows_at(it + gridDim.x, x1));
+    resolve_store(1);
+    __syncthreads();
+  }
+  load_k(cur, cn, 0);
+  load_v(cur, cn, 0);
   while (it < items) {
     const int64_t it_next = it + gridDim.x;
-    const Item nxt = item_of(it_next < items ? it_next : items - 1, rows, kv_heads);
-    const int cn_next = it_next < items ? chunk_rows(nxt) : 0;
+    const int64_t it_next2 = it_next + gridDim.x;
+    const Item nxt = item_at(it_next);
+    const int cn_next = rows_at(it_next, nxt);
+    const Item nxt2 = item_at(it_next2);
+    const int cn_next2 = rows_at(it_next2, nxt2);
+    const int rs_cur = FUSED ? j % 3 : 0, rs_next = FUSED ? (j + 1) % 3 : 0;
     // An item with no rows (cn == 0) runs the same code on masked rows and
     // skips its stores, so every prefetch is issued from one program point.
     {
-      // stage this item's K in LDS (rows past the width are zero)
+      // stage this item's K in LDS (rows past the width are zero; rows whose
+      // ID or slot was out of range are NaN, as in the compact path)
       __syncthreads();  // the previous item is done with LDS
 #pragma unroll
       for (int r = 0; r < KV4; ++r) {
         const int e = tid + r * NT;
         const int i = e / (D / 4);
         const int c = e - i * (D / 4);
-        smem4[(i * KP) / 4 + c] = i < cn ? kst[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 kv = i < cn ? kst[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (FUSED) {
+          if (i < cn && ring[rs_cur][i] < 0) {
+            const float nan = __int_as_float(0x7fc00000);
+            kv = make_float4(nan, nan, nan, nan);
+          }
+        }
+        smem4[(i * KP) / 4 + c] = kv;
       }
       __syncthreads();
       // next item's K streams in under this item; the scheduling barriers keep
       // the compiler from hoisting it (or V below) above the last use of the
       // registers it refills, which would double the register footprint
       __builtin_amdgcn_sched_barrier(0);
-      load_k(nxt, cn_next);
+      load_k(nxt, cn_next, rs_next);
+      resolve_ids(nxt2, cn_next2);
 
       // scores for this wavefront's query heads: lane = compact row
       const int64_t row = row0 + cur.lrow;
+      // with GQ < 4 the wavefronts past the last head only clamp their head
+      // index (in bounds) and discard the result
       const float* qrow[HPW];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
-        qrow[hh] = q + (row * q_heads + (int64_t)cur.hk * GQ + wave * HPW + hh) * D;
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int hl = wave * HPW + hh < GQ ? wave * HPW + hh : GQ - 1;
+        qrow[hh] = q + (row * q_heads + (int64_t)cur.hk * GQ + hl) * D;
+      }
       float dot[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) dot[hh] = 0.0f;
@@ -183,11 +271,13 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
         const float m = wave_max(sc);
         const float p = (lane < cn) ? expf(sc - m) : 0.0f;
         const float l = wave_sum(p);
+        if (wave * HPW + hh >= GQ) continue;  // uniform: no such head
         ps[(wave * HPW + hh) * C + lane] = p;
         if (lane == 0 && cn > 0)
           *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)(wave * HPW + hh) * n_chunks) * 2) =
               make_float2(m, l);
       }
+      resolve_slots(nxt2, cn_next2);
       __syncthreads();  // ps complete; K no longer read, so smem can hold partials
 
       // P.V over this wavefront's rows, in row order; lane owns dims lane*DPL..
@@ -215,7 +305,7 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_v(nxt, cn_next);  // next item's V streams in under the rest
+      load_v(nxt, cn_next, rs_next);  // next item's V streams in under the rest
 
       // combine the wavefronts' partial sums in wavefront order
       if constexpr (NW == 1) {
@@ -240,10 +330,12 @@ attend_chunk_kernel(const float* __restrict__ q, const float* __restrict__ k_com
           part_acc[(slot0 + (int64_t)h * n_chunks) * D + d] = sum;
         }
       }
+      resolve_store(FUSED ? (j + 2) % 3 : 0);  // visible after the next item's first barrier
     }
     it = it_next;
     cur = nxt;
     cn = cn_next;
+    ++j;
   }
 }
 
@@ -338,34 +430,42 @@ int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-template <int D, int GQ>
+template <int D, int GQ, bool FUSED>
 hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
   using A = AttnCfg<D, GQ>;
   static int per_cu = 0;  // resident workgroups per compute unit for this instance
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ>, A::NT, 0) !=
-            hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ, FUSED>, A::NT,
+                                                     0) != hipSuccess ||
+        n < 1)
       n = 1;
     per_cu = n;
   }
   const int64_t items = (int64_t)a.n_chunks * a.rows * a.kv_heads;
   const int64_t slots = (int64_t)device_cus() * per_cu;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
-  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ>), dim3(grid), dim3(A::NT), 0, s, a.q,
-                     a.k_compact, a.v_compact, a.width, a.q_heads, a.kv_heads, a.stride,
-                     a.n_chunks, a.scale, a.row0, a.rows, a.part_acc, a.part_ml);
+  RowSource src{a.k_compact, a.v_compact, a.token_ids, a.seq_len, a.slot_map, a.slot_off,
+                a.k_cache, a.v_cache, a.kv_slots, a.queries};
+  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ, FUSED>), dim3(grid), dim3(A::NT), 0, s, a.q, src,
+                     a.width, a.q_heads, a.kv_heads, a.stride, a.n_chunks, a.scale, a.row0,
+                     a.rows, a.part_acc, a.part_ml);
   return hipGetLastError();
+}
+
+template <int D, int GQ>
+hipError_t launch_attend_f(const AttendArgs& a, hipStream_t s) {
+  return a.token_ids ? launch_attend_t<D, GQ, true>(a, s) : launch_attend_t<D, GQ, false>(a, s);
 }
 
 template <int D>
 hipError_t launch_attend_d(const AttendArgs& a, hipStream_t s) {
   switch (a.q_heads / a.kv_heads) {
-    case 1: return launch_attend_t<D, 1>(a, s);
-    case 2: return launch_attend_t<D, 2>(a, s);
-    case 4: return launch_attend_t<D, 4>(a, s);
-    case 8: return launch_attend_t<D, 8>(a, s);
-    case 16: return launch_attend_t<D, 16>(a, s);
+    case 1: return launch_attend_f<D, 1>(a, s);
+    case 2: return launch_attend_f<D, 2>(a, s);
+    case 4: return launch_attend_f<D, 4>(a, s);
+    case 8: return launch_attend_f<D, 8>(a, s);
+    case 16: return launch_attend_f<D, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -157,7 +157,7 @@ struct GatherArgs {
 
 struct AttendArgs {
   const float* q;            // global rows
-  const float* k_compact;    // local rows
+  const float* k_compact;    // local rows (compact path)
   const float* v_compact;
   const int32_t* width;      // global rows
   int32_t q_heads;
@@ -172,6 +172,16 @@ struct AttendArgs {
   float* part_ml;            // [rows][H_q][n_chunks][2]
   float* out;                // global rows
   float* lse;                // global rows, may be null
+  // fused path (token_ids != null): rows are read from the cache through the
+  // slot map instead of the compact scratch
+  const int32_t* token_ids = nullptr;  // global rows
+  const int32_t* seq_len = nullptr;
+  const int32_t* slot_map = nullptr;
+  const int64_t* slot_off = nullptr;
+  const float* k_cache = nullptr;
+  const float* v_cache = nullptr;
+  int64_t kv_slots = 0;
+  int32_t queries = 1;
 };
 
 struct ChunkArgs {
