@@ -251,6 +251,21 @@ QSA_API int qsa_decode_fused(const qsa_shape *shape, const float *index_q, const
                              float *lse, void *workspace, size_t workspace_bytes,
                              qsa_timer *timer, qsa_stream stream);
 
+/* The bounded dense causal row on the GPU: every visible token 0..N-1, in
+ * order, resolved through the slot map and attended with exactly the
+ * reduction order of step 8, for rows with N <= 4k+3 ([SET] §The
+ * dense-parity property: at or below the budget the sparse row is this row,
+ * so qsa_decode and this call return the same bits there; [MASK] §Failure
+ * boundary: the dense oracle is bounded at 2,051 keys for k = 512).  Rows
+ * with more visible tokens get width -1 and NaN outputs.  Writes token_ids
+ * ([rows][4k+4], the dense row) and width; needs qsa_workspace_bytes. */
+QSA_API int qsa_dense_attend(const qsa_shape *shape, const int32_t *seq_len,
+                             const int32_t *slot_map, const int64_t *slot_off,
+                             const float *k_cache, const float *v_cache, const float *q,
+                             float softmax_scale, int32_t *token_ids, int32_t *width, float *out,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             qsa_stream stream);
+
 /* Host-only byte ledger for a cache of total_tokens tokens ([MASK] §What
  * the checkpoint measures; the dense-mask count is always 0). */
 QSA_API int qsa_accounting(const qsa_shape *shape, int64_t total_tokens, qsa_bytes *out_host);

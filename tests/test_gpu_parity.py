@@ -352,3 +352,43 @@ def test_fused_chunk_rows_equal_compact():
     fused = _fused_copy(case)
     assert torch.equal(fused.token_ids, case.token_ids)
     assert torch.equal(fused.out, case.out) and torch.equal(fused.lse, case.lse)
+
+
+# ------------------------------------------------------------ dense GPU row
+
+def test_dense_gpu_row_equals_sparse_below_budget():
+    """At or below the budget the sparse GPU row and the bounded dense GPU row
+    are the same row in the same order, so their outputs are equal bit for
+    bit; one group past the cut the dense row is refused (width -1)."""
+    lens = inputs.sweep_prefixes()
+    spec = inputs.custom("dense", lens, h_i=4, d_i=32, h_q=4, h_kv=2, d=128, keys="grid",
+                         slots="perm")
+    data = inputs.make(spec, seed=8, device="cpu")
+    case = harness.GpuCase(data)
+    case.decode()
+    ids = torch.empty_like(case.token_ids)
+    width = torch.empty_like(case.width)
+    out = torch.empty_like(case.out)
+    lse = torch.empty_like(case.lse)
+    qsa.qsa_dense_attend(case.shape, case.seq_len, case.slot_map, case.slot_off, case.k_cache,
+                         case.v_cache, case.q, case.scale, ids, width, out, lse, case.workspace)
+    torch.cuda.synchronize()
+    for r, n in enumerate(lens):
+        if n <= 2051:
+            assert int(width[r]) == n
+            assert torch.equal(ids[r], case.token_ids[r])
+            assert torch.equal(out[r], case.out[r]) and torch.equal(lse[r], case.lse[r])
+        else:
+            assert int(width[r]) == -1 and torch.isnan(out[r]).all()
+    # and the dense rows against the oracle's dense row
+    for r, n in enumerate(lens):
+        if 0 < n <= 2051:
+            dense = oracle.dense_row(n, data["slot_map"].numpy()[int(data["raw_off"][r]):],
+                                     data["kv_slots"], data["k_cache"].numpy(),
+                                     data["v_cache"].numpy(), data["q"][r].numpy(), case.scale)
+            kx, vx = oracle.gather(oracle.resolve(dense["ids"],
+                                                  data["slot_map"].numpy()[int(data["raw_off"][r]):],
+                                                  data["kv_slots"]),
+                                   data["k_cache"].numpy(), data["v_cache"].numpy())
+            ex, _ = oracle.attend_exact(data["q"][r].numpy(), kx, vx, case.scale)
+            assert harness.normwise_rel_err(out[r].cpu().numpy(), ex) <= 2e-6

@@ -99,6 +99,7 @@ def lib():
                            ctypes.c_int),
             "qsa_decode_fused": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
                                  ctypes.c_int),
+            "qsa_dense_attend": ([S, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
             "qsa_accounting": ([S, i64, ctypes.POINTER(Bytes)], ctypes.c_int),
             "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "qsa_version": ([], ctypes.c_char_p),
@@ -233,6 +234,19 @@ def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, 
 def qsa_decode_fused(*args, **kw):
     """qsa_decode with the gather fused into the attention (no compact scratch)."""
     return qsa_decode(*args, fused=True, **kw)
+
+
+def qsa_dense_attend(shape, seq_len, slot_map, slot_off, k_cache, v_cache, q, softmax_scale,
+                     token_ids, width, out, lse, workspace, stream=None):
+    _check(lib().qsa_dense_attend(
+        ctypes.byref(shape), _ptr(seq_len, torch.int32, "seq_len"),
+        _ptr(slot_map, torch.int32, "slot_map"), _ptr(slot_off, torch.int64, "slot_off"),
+        _ptr(k_cache, torch.float32, "k_cache"), _ptr(v_cache, torch.float32, "v_cache"),
+        _ptr(q, torch.float32, "q"), ctypes.c_float(softmax_scale),
+        _ptr(token_ids, torch.int32, "token_ids"), _ptr(width, torch.int32, "width"),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", True),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "qsa_dense_attend")
 
 
 def qsa_accounting(shape, total_tokens):

@@ -396,6 +396,46 @@ static int decode_impl(bool fused, const qsa_shape* s, const float* index_q, con
 
 extern "C" {
 
+int qsa_dense_attend(const qsa_shape* s, const int32_t* seq_len, const int32_t* slot_map,
+                     const int64_t* slot_off, const float* k_cache, const float* v_cache,
+                     const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
+                     float* out, float* lse, void* ws, size_t ws_bytes, qsa_stream stream) {
+  int rc = validate(s, kNeedAttn | kNeedBudget);
+  if (rc != QSA_OK) return rc;
+  if (!seq_len || !slot_map || !slot_off || !k_cache || !v_cache || !q || !token_ids || !width ||
+      !out || !ws)
+    return QSA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out) ||
+      !aligned16(token_ids) || !aligned16(ws))
+    return QSA_ERR_SHAPE;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = row_count(s), R = rows_per_pass(s);
+  if (launch_dense_ids(seq_len, s->queries, s->budget_groups, rows, token_ids, width, st) !=
+      hipSuccess)
+    return QSA_ERR_HIP;
+  char* w = (char*)ws;
+  for (int64_t r0 = 0; r0 < rows; r0 += R) {
+    const int64_t n = (rows - r0) < R ? (rows - r0) : R;
+    AttendArgs aa{q, nullptr, nullptr, width, s->q_heads, s->kv_heads, s->head_dim,
+                  token_stride(s), attn_chunks(s), softmax_scale, r0, n,
+                  reinterpret_cast<float*>(w + L.pacc), reinterpret_cast<float*>(w + L.pml), out,
+                  lse};
+    aa.token_ids = token_ids;
+    aa.seq_len = seq_len;
+    aa.slot_map = slot_map;
+    aa.slot_off = slot_off;
+    aa.k_cache = k_cache;
+    aa.v_cache = v_cache;
+    aa.kv_slots = s->kv_slots;
+    aa.queries = s->queries;
+    if (launch_attend(aa, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_merge(aa, st) != hipSuccess) return QSA_ERR_HIP;
+  }
+  return QSA_OK;
+}
+
 int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
                const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
                const int64_t* slot_off, const float* k_cache, const float* v_cache,

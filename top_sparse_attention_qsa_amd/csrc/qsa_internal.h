@@ -232,6 +232,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, int64_t rows,
+                            int32_t* token_ids, int32_t* width, hipStream_t s);
 bool chunk_supported(int h_i, int queries, int64_t rows_per_launch);
 hipError_t launch_chunk(const ChunkArgs& a, int h_i, int d_i, hipStream_t s);
 hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hipStream_t s);

@@ -497,7 +497,32 @@ emit_kernel(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ seq
   if (tid == 0) width[row] = w;
 }
 
+// The bounded dense row: every visible token 0..N-1 in order, for rows with
+// at most 4k+3 visible tokens (AFN-017 §The dense-parity property: below the
+// cut the sparse row is exactly this row; AFN-016 §Failure boundary: the
+// dense oracle is bounded at 2,051 keys).  Longer or invalid rows get width -1.
+__global__ void __launch_bounds__(256)
+dense_ids_kernel(const int32_t* __restrict__ seq_len, int32_t queries, int32_t k,
+                 int32_t* __restrict__ token_ids, int32_t* __restrict__ width) {
+  const int64_t row = blockIdx.x;
+  const int32_t stride = 4 * k + 4;
+  const int32_t b = (int32_t)(row / queries);
+  const int64_t n = (int64_t)seq_len[b] - queries + 1 + (row - (int64_t)b * queries);
+  const bool ok = n >= 0 && n <= 4 * (int64_t)k + 3;
+  int32_t* ids = token_ids + row * stride;
+  for (int i = (int)threadIdx.x; i < stride; i += 256) ids[i] = (ok && i < n) ? i : -1;
+  if (threadIdx.x == 0) width[row] = ok ? (int32_t)n : -1;
+}
+
 }  // namespace
+
+hipError_t launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, int64_t rows,
+                            int32_t* token_ids, int32_t* width, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(dense_ids_kernel, dim3((unsigned)rows), dim3(256), 0, s, seq_len, queries, k,
+                     token_ids, width);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
