@@ -71,18 +71,36 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
-// Butterfly reductions: every lane ends with the same value, reduced in a
-// fixed order independent of timing.
+// Wavefront reductions.  Within each 16-lane DPP row, rotations by 1, 2, 4
+// and 8 lanes (row_ror) leave every lane holding its row's reduction; lane 0
+// of each row is then read into a scalar and the four rows are combined as
+// (r0 op r1) op (r2 op r3).  The order is fixed, so a sum is the same bits on
+// every run and the result is uniform across the wavefront.  DPP stays in
+// the VALU: no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kRowRor1>(v));
+  v = fmaxf(v, dpp_f32<kRowRor2>(v));
+  v = fmaxf(v, dpp_f32<kRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kRowRor8>(v));
+  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = v + __shfl_xor(v, o, kWave);
-  return v;
+  v = v + dpp_f32<kRowRor1>(v);
+  v = v + dpp_f32<kRowRor2>(v);
+  v = v + dpp_f32<kRowRor4>(v);
+  v = v + dpp_f32<kRowRor8>(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 // Exclusive prefix sum over a whole workgroup of NT threads (NT/64 waves);
