@@ -128,6 +128,55 @@ def cpu_baseline(data, rows, threads):
                 seconds=timed)
 
 
+def chunk_leg(seed, steps):
+    """Causal chunks: 8 sequences of lengths drawn from [2,051, 262,144], 256
+    queries each (2,048 rows, rows_in_flight 256), indexer 16 x 128, attention
+    32 q / 4 KV x 128.  Times one qsa_decode call over all rows with the
+    per-row compact gather, the union gather and the fused attention, checks
+    the three give identical bits, and counts the K/V rows each one copies."""
+    import numpy as np
+    import torch
+    from tests import harness, inputs
+    spec = inputs.spec("c5", seed=seed)
+    data = inputs.make(spec, seed=seed, device="cuda")
+    case = harness.GpuCase(data, rows_in_flight=256)
+    rows = spec.rows
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    res, ref = {}, None
+    for mode in ("compact", "dedup", "fused"):
+        case.decode(rows=mode)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            case.decode(rows=mode)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / steps
+        got = case.results()
+        if ref is None:
+            ref = got
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"{mode} differs"
+        res[mode] = {"ms_per_step": ms, "rows_per_s": rows / (ms * 1e-3)}
+    ids = ref[0].cpu().numpy()
+    width = ref[1].cpu().numpy()
+    union_groups = 0
+    for b in range(spec.batch):
+        blk = ids[b * spec.queries:(b + 1) * spec.queries]
+        union_groups += len(np.unique(blk[blk >= 0] // 4))
+    kv_row = spec.h_kv * spec.d * 4
+    res["compact"]["kv_rows_copied"] = int(width.sum())
+    res["dedup"]["kv_rows_copied"] = 4 * union_groups
+    res["fused"]["kv_rows_copied"] = 0
+    for m in ("compact", "dedup"):
+        res[m]["kv_copy_bytes"] = 2 * 2 * kv_row * res[m]["kv_rows_copied"]  # K+V, read+write
+    return {"workload": "causal chunks: 8 sequences, lengths U[2,051, 262,144] (seeded), 256 "
+                        "queries each, budget 512, indexer 16 x 128, attention 32 q / 4 KV x "
+                        "128, identity slot maps, 256 rows in flight",
+            "rows": rows, "steps": steps, **res}
+
+
 def copy_calibration(gib=1.0, reps=5):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -147,6 +196,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true",
+                    help="skip the causal-chunk leg (compact vs union gather vs fused)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter scale factor)")
     args = ap.parse_args()
@@ -274,6 +325,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_chunk:
+        print("[bench] chunk leg", file=sys.stderr, flush=True)
+        result["chunk"] = chunk_leg(args.seed, steps=5)
     if keep_raw:
         threads = len(os.sched_getaffinity(0))
         threads = max(1, min(threads, 16, rows))

@@ -266,6 +266,59 @@ QSA_API int qsa_dense_attend(const qsa_shape *shape, const int32_t *seq_len,
                              float *lse, void *workspace, size_t workspace_bytes,
                              qsa_stream stream);
 
+/* Steps 6-7 once per chunk instead of once per row.  The queries of a
+ * causal chunk choose nearly the same groups, so the union of the groups
+ * their IDs touch (selected groups and each row's raw-tail group) is
+ * resolved through the slot map and copied once, into a union scratch
+ * ([MASK] §Decision: only the gather crosses into physical layout; §Why
+ * compact gather comes before fusion: one explicit copy into bounded
+ * scratch; [SET] capsule evidence: chunk/decode equality).  All rows form one
+ * union, so rows_in_flight must be 0 or at least batch x queries
+ * (QSA_ERR_UNSUPPORTED otherwise).
+ *   k_union, v_union  [rows x (4k+4)][H_kv][D] f32 (the compact capacity; a
+ *                     union never needs more).  Union group u (groups
+ *                     ordered by sequence, then position) occupies rows
+ *                     4u..4u+3, token 4g+e at row 4u+e.  Tokens that no row
+ *                     of the sequence can see are left unwritten; an
+ *                     out-of-range slot gives a NaN row.
+ *   union_pos         [rows][4k+4] int32: row i of a query row is scratch row
+ *                     union_pos[row][i]; -1 past the width and for IDs the
+ *                     row cannot see.
+ *   union_groups      device int32, receives the union's group count; may be
+ *                     NULL.
+ * Needs qsa_workspace_bytes(shape). */
+QSA_API int qsa_union_gather(const qsa_shape *shape, const int32_t *token_ids,
+                             const int32_t *width, const int32_t *seq_len,
+                             const int32_t *slot_map, const int64_t *slot_off,
+                             const float *k_cache, const float *v_cache, float *k_union,
+                             float *v_union, int32_t *union_pos, int32_t *union_groups,
+                             void *workspace, size_t workspace_bytes, qsa_stream stream);
+
+/* Step 8 over rows read through a position list: row i of query row r is
+ * k_rows/v_rows row row_pos[r][i] ([rows][4k+4] int32; rows [n_rows][H_kv][D]
+ * f32).  A position outside [0, n_rows) makes that row NaN.  Same chunked
+ * chronological order and bits as qsa_online_attend over the equivalent
+ * compact rows.  Needs qsa_workspace_bytes(shape). */
+QSA_API int qsa_online_attend_indexed(const qsa_shape *shape, const float *q,
+                                      const float *k_rows, const float *v_rows, int64_t n_rows,
+                                      const int32_t *row_pos, const int32_t *width,
+                                      float softmax_scale, float *out, float *lse,
+                                      void *workspace, size_t workspace_bytes,
+                                      qsa_stream stream);
+
+/* Steps 1-8 with the union gather: per pass of rows_in_flight rows, one
+ * union of the rows' K/V (as qsa_union_gather, per pass) replaces the
+ * per-row compact copies, and the attention reads each row through its
+ * position list.  Same arguments, workspace and results as qsa_decode, bit
+ * for bit; for decode rows (queries = 1) the union is each row's own rows. */
+QSA_API int qsa_decode_dedup(const qsa_shape *shape, const float *index_q, const float *pooled,
+                             const int64_t *pooled_off, const int32_t *seq_len,
+                             const int32_t *slot_map, const int64_t *slot_off,
+                             const float *k_cache, const float *v_cache, const float *q,
+                             float softmax_scale, int32_t *token_ids, int32_t *width, float *out,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             qsa_timer *timer, qsa_stream stream);
+
 /* Host-only byte ledger for a cache of total_tokens tokens ([MASK] §What
  * the checkpoint measures; the dense-mask count is always 0). */
 QSA_API int qsa_accounting(const qsa_shape *shape, int64_t total_tokens, qsa_bytes *out_host);

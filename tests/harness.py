@@ -54,11 +54,16 @@ class GpuCase:
         self.out = torch.empty((rows, s.h_q, s.d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((rows, s.h_q), dtype=torch.float32, device=dev)
 
-    def decode(self, timer=None, fused=False):
+    def decode(self, timer=None, fused=False, rows="compact"):
+        """Steps 1-8; rows = "compact", "fused" or "dedup" (how K/V are read)."""
         qsa.qsa_decode(self.shape, self.index_q, self.pooled, self.pooled_off, self.seq_len,
                        self.slot_map, self.slot_off, self.k_cache, self.v_cache, self.q,
                        self.scale, self.token_ids, self.width, self.out, self.lse,
-                       self.workspace, timer, fused=fused)
+                       self.workspace, timer, fused=fused, rows=rows)
+
+    def results(self):
+        """Clones of (token_ids, width, out, lse)."""
+        return (self.token_ids.clone(), self.width.clone(), self.out.clone(), self.lse.clone())
 
 
 def host(t):

@@ -29,7 +29,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     L = qsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -52,7 +52,11 @@ def test_workspace_scales_with_groups_and_width_never_tokens():
     per_row_compact = 2 * (4 * 512 + 4) * 4 * 128 * 4
     per_row_groups = 65536 * 4 + 65536 // 16 * 4
     per_row_part = 32 * 33 * (128 + 2) * 4
-    assert base <= 32 * (per_row_compact + per_row_groups + per_row_part) + 6 * 256
+    # union gather: row bitmap, union bitmap and word prefixes (at most one
+    # sequence per row), union list, position list
+    per_row_union = 3 * (65536 // 32 + 1) * 4 + 513 * 8 + (4 * 512 + 4) * 4
+    assert base <= 32 * (per_row_compact + per_row_groups + per_row_part + per_row_union) + \
+        16 * 256
     # bounding rows in flight bounds the workspace
     small = qsa.qsa_workspace_bytes(shape(rows_in_flight=4))
     assert small * 7 < base
@@ -109,6 +113,16 @@ def test_null_pointers_and_small_workspace_rejected():
                         ctypes.c_size_t(10), None, None) == qsa.QSA_ERR_WORKSPACE
     assert L.qsa_decode(None, *([p] * 9), ctypes.c_float(0.1), p, p, p, None, p,
                         ctypes.c_size_t(1 << 40), None, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_decode_dedup(ctypes.byref(s), *([p] * 9), ctypes.c_float(0.1), p, p, p, None,
+                              p, ctypes.c_size_t(10), None, None) == qsa.QSA_ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 40)
+    assert L.qsa_union_gather(ctypes.byref(s), p, p, p, p, p, p, p, p, p, None, None, p, big,
+                              None) == qsa.QSA_ERR_NULL
+    split = shape(rows_in_flight=4)  # one union needs every row in one pass
+    assert L.qsa_union_gather(ctypes.byref(split), p, p, p, p, p, p, p, p, p, p, None, p, big,
+                              None) == qsa.QSA_ERR_UNSUPPORTED
+    assert L.qsa_online_attend_indexed(ctypes.byref(s), p, p, p, 0, p, p, ctypes.c_float(1.0),
+                                       p, None, p, big, None) == qsa.QSA_ERR_SHAPE
     # misaligned device pointers are refused, not dereferenced
     odd = ctypes.c_void_p(258)
     assert L.qsa_score_groups(ctypes.byref(s), p, odd, p, p, p, None) == qsa.QSA_ERR_SHAPE

@@ -121,13 +121,18 @@ def test_chunk_all_tied_streaming_path():
 def test_c5_chunk_equals_256_single_query_decodes():
     """8 sequences of lengths drawn from [2,051, 262,144] (plus the 2,051
     boundary), 256 causal queries each, indexer 16 x 128, attention 32 q /
-    4 KV x 128: chunk results equal 256 sequential decodes per sequence."""
+    4 KV x 128: chunk results, with per-row compact gathers and with one
+    union gather per sequence, equal 256 sequential decodes per sequence."""
     spec = inputs.spec("c5", seed=1)
     spec.seq_lens[0] = 2051 + 255          # first row sees exactly 2,051 tokens
     data = inputs.make(spec, seed=1, device="cuda")
     case = harness.GpuCase(data, rows_in_flight=256)
     case.decode()
-    assert_same(case, decode_per_row(case, rows_in_flight=256))
+    ref = decode_per_row(case, rows_in_flight=256)
+    assert_same(case, ref)
+    # one union gather per pass of 256 rows gives the same bits
+    case.decode(rows="dedup")
+    assert_same(case, ref)
     assert int(case.width[0]) == 2051     # boundary row: dense, 512 groups + 3 tail
     fetch = harness.device_kv_fetch(case.k_cache, case.v_cache)
     ids = case.token_ids.cpu().numpy()

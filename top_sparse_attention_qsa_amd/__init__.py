@@ -100,6 +100,11 @@ def lib():
             "qsa_decode_fused": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
                                  ctypes.c_int),
             "qsa_dense_attend": ([S, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
+            "qsa_union_gather": ([S, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+            "qsa_online_attend_indexed": ([S, P, P, P, i64, P, P, f32, P, P, P, sz, P],
+                                          ctypes.c_int),
+            "qsa_decode_dedup": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
+                                 ctypes.c_int),
             "qsa_accounting": ([S, i64, ctypes.POINTER(Bytes)], ctypes.c_int),
             "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "qsa_version": ([], ctypes.c_char_p),
@@ -214,10 +219,18 @@ def qsa_online_attend(shape, q, k_compact, v_compact, width, softmax_scale, out,
         "qsa_online_attend")
 
 
+_DECODE_VARIANTS = {"compact": "qsa_decode", "fused": "qsa_decode_fused",
+                    "dedup": "qsa_decode_dedup"}
+
+
 def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
                v_cache, q, softmax_scale, token_ids, width, out, lse, workspace, timer=None,
-               stream=None, fused=False):
-    fn = lib().qsa_decode_fused if fused else lib().qsa_decode
+               stream=None, fused=False, rows="compact"):
+    """Steps 1-8.  rows selects how steps 6-8 read K/V: "compact" (per-row
+    gather), "fused" (slot-map loads inside the attention; also fused=True)
+    or "dedup" (one union gather per pass)."""
+    name = _DECODE_VARIANTS["fused" if fused else rows]
+    fn = getattr(lib(), name)
     _check(fn(
         ctypes.byref(shape), _ptr(index_q, torch.float32, "index_q"),
         _ptr(pooled, torch.float32, "pooled"), _ptr(pooled_off, torch.int64, "pooled_off"),
@@ -228,12 +241,46 @@ def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, 
         _ptr(width, torch.int32, "width"), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse", True), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), timer.handle if timer is not None else None, _stream(stream)),
-        "qsa_decode_fused" if fused else "qsa_decode")
+        name)
 
 
 def qsa_decode_fused(*args, **kw):
     """qsa_decode with the gather fused into the attention (no compact scratch)."""
     return qsa_decode(*args, fused=True, **kw)
+
+
+def qsa_decode_dedup(*args, **kw):
+    """qsa_decode with one union gather per pass of rows."""
+    return qsa_decode(*args, rows="dedup", **kw)
+
+
+def qsa_union_gather(shape, token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache,
+                     k_union, v_union, union_pos, union_groups, workspace, stream=None):
+    _check(lib().qsa_union_gather(
+        ctypes.byref(shape), _ptr(token_ids, torch.int32, "token_ids"),
+        _ptr(width, torch.int32, "width"), _ptr(seq_len, torch.int32, "seq_len"),
+        _ptr(slot_map, torch.int32, "slot_map"), _ptr(slot_off, torch.int64, "slot_off"),
+        _ptr(k_cache, torch.float32, "k_cache"), _ptr(v_cache, torch.float32, "v_cache"),
+        _ptr(k_union, torch.float32, "k_union"), _ptr(v_union, torch.float32, "v_union"),
+        _ptr(union_pos, torch.int32, "union_pos"),
+        _ptr(union_groups, torch.int32, "union_groups", True),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "qsa_union_gather")
+
+
+def qsa_online_attend_indexed(shape, q, k_rows, v_rows, row_pos, width, softmax_scale, out, lse,
+                              workspace, stream=None):
+    n_rows = k_rows.shape[0]
+    if v_rows.shape[0] != n_rows:
+        raise ValueError("k_rows and v_rows differ in row count")
+    _check(lib().qsa_online_attend_indexed(
+        ctypes.byref(shape), _ptr(q, torch.float32, "q"), _ptr(k_rows, torch.float32, "k_rows"),
+        _ptr(v_rows, torch.float32, "v_rows"), int(n_rows),
+        _ptr(row_pos, torch.int32, "row_pos"), _ptr(width, torch.int32, "width"),
+        ctypes.c_float(softmax_scale), _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse", True), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)),
+        "qsa_online_attend_indexed")
 
 
 def qsa_dense_attend(shape, seq_len, slot_map, slot_off, k_cache, v_cache, q, softmax_scale,

@@ -65,7 +65,9 @@ int validate(const qsa_shape* s, int need) {
 }
 
 struct Layout {
-  size_t scores, maxima, kc, vc, pacc, pml, total;
+  size_t scores, maxima, kc, vc, pacc, pml;
+  size_t rbm, ubm, upre, ublk, ulist, upos;  // union gather (chunk dedup)
+  size_t total;
 };
 
 Layout layout(const qsa_shape* s) {
@@ -87,6 +89,20 @@ Layout layout(const qsa_shape* s) {
   off = align256(off + slots * s->head_dim * sizeof(float));
   L.pml = off;
   off = align256(off + slots * 2 * sizeof(float));
+  const int64_t wps = union_words_per_seq(g);
+  const int64_t useq = union_seqs_per_pass(R, s->queries, s->batch);
+  L.rbm = off;
+  off = align256(off + (size_t)R * wps * sizeof(uint32_t));
+  L.ubm = off;
+  off = align256(off + (size_t)useq * wps * sizeof(uint32_t));
+  L.upre = off;
+  off = align256(off + (size_t)useq * wps * sizeof(uint32_t));
+  L.ublk = off;
+  off = align256(off + (size_t)(union_scan_blocks(useq * wps) + 1) * sizeof(uint32_t));
+  L.ulist = off;
+  off = align256(off + (size_t)R * (s->budget_groups + 1) * sizeof(int2));
+  L.upos = off;
+  off = align256(off + (size_t)R * token_stride(s) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -310,7 +326,44 @@ void qsa_timer_destroy(qsa_timer* t) {
 
 }  // extern "C"
 
-static int decode_impl(bool fused, const qsa_shape* s, const float* index_q, const float* pooled,
+// How steps 6-8 read the selected K/V rows.
+enum class Rows { kCompact, kFused, kUnion };
+
+static UnionArgs union_args(const qsa_shape* s, const Layout& L, char* w, const int32_t* token_ids,
+                            const int32_t* width, const int32_t* seq_len, const int32_t* slot_map,
+                            const int64_t* slot_off, const float* k_cache, const float* v_cache,
+                            int64_t r0, int64_t n, float* k_union, float* v_union,
+                            int32_t* union_pos, int32_t* count_out) {
+  UnionArgs u{};
+  u.token_ids = token_ids;
+  u.width = width;
+  u.seq_len = seq_len;
+  u.slot_map = slot_map;
+  u.slot_off = slot_off;
+  u.k_cache = k_cache;
+  u.v_cache = v_cache;
+  u.queries = s->queries;
+  u.kv_heads = s->kv_heads;
+  u.head_dim = s->head_dim;
+  u.stride = token_stride(s);
+  u.kv_slots = s->kv_slots;
+  u.max_groups = s->max_groups;
+  u.row0 = r0;
+  u.rows = n;
+  u.cus = device_cus();
+  u.row_bitmap = reinterpret_cast<uint32_t*>(w + L.rbm);
+  u.union_bitmap = reinterpret_cast<uint32_t*>(w + L.ubm);
+  u.word_prefix = reinterpret_cast<uint32_t*>(w + L.upre);
+  u.block_prefix = reinterpret_cast<uint32_t*>(w + L.ublk);
+  u.union_list = reinterpret_cast<int2*>(w + L.ulist);
+  u.k_union = k_union;
+  u.v_union = v_union;
+  u.union_pos = union_pos;
+  u.count_out = count_out;
+  return u;
+}
+
+static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, const float* pooled,
                const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
                const int64_t* slot_off, const float* k_cache, const float* v_cache,
                const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
@@ -365,16 +418,26 @@ static int decode_impl(bool fused, const qsa_shape* s, const float* index_q, con
       return QSA_ERR_HIP;
     }
     if (timed && hipEventRecord(ev[2], st) != hipSuccess) return QSA_ERR_HIP;
-    if (!fused) {
+    int32_t* upos = reinterpret_cast<int32_t*>(w + L.upos);
+    if (mode == Rows::kCompact) {
       GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
                     s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, r0, n, kc, vc,
                     nullptr};
       if (launch_gather(ga, st) != hipSuccess) return QSA_ERR_HIP;
+    } else if (mode == Rows::kUnion) {
+      const UnionArgs ua = union_args(s, L, w, token_ids, width, seq_len, slot_map, slot_off,
+                                      k_cache, v_cache, r0, n, kc, vc, upos, nullptr);
+      if (launch_union(ua, st) != hipSuccess) return QSA_ERR_HIP;
     }
     if (timed && hipEventRecord(ev[3], st) != hipSuccess) return QSA_ERR_HIP;
     AttendArgs aa{q, kc, vc, width, s->q_heads, s->kv_heads, s->head_dim, token_stride(s),
                   attn_chunks(s), softmax_scale, r0, n, pacc, pml, out, lse};
-    if (fused) {
+    if (mode == Rows::kUnion) {
+      aa.union_pos = upos;
+      aa.k_cache = kc;
+      aa.v_cache = vc;
+      aa.kv_slots = n * (int64_t)token_stride(s);
+    } else if (mode == Rows::kFused) {
       aa.token_ids = token_ids;
       aa.seq_len = seq_len;
       aa.slot_map = slot_map;
@@ -442,7 +505,7 @@ int qsa_decode(const qsa_shape* s, const float* index_q, const float* pooled,
                const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
                float* out, float* lse, void* ws, size_t ws_bytes, qsa_timer* timer,
                qsa_stream stream) {
-  return decode_impl(false, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
+  return decode_impl(Rows::kCompact, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
                      v_cache, q, softmax_scale, token_ids, width, out, lse, ws, ws_bytes, timer,
                      stream);
 }
@@ -453,9 +516,71 @@ int qsa_decode_fused(const qsa_shape* s, const float* index_q, const float* pool
                      const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
                      float* out, float* lse, void* ws, size_t ws_bytes, qsa_timer* timer,
                      qsa_stream stream) {
-  return decode_impl(true, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
+  return decode_impl(Rows::kFused, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, k_cache,
                      v_cache, q, softmax_scale, token_ids, width, out, lse, ws, ws_bytes, timer,
                      stream);
+}
+
+int qsa_decode_dedup(const qsa_shape* s, const float* index_q, const float* pooled,
+                     const int64_t* pooled_off, const int32_t* seq_len, const int32_t* slot_map,
+                     const int64_t* slot_off, const float* k_cache, const float* v_cache,
+                     const float* q, float softmax_scale, int32_t* token_ids, int32_t* width,
+                     float* out, float* lse, void* ws, size_t ws_bytes, qsa_timer* timer,
+                     qsa_stream stream) {
+  return decode_impl(Rows::kUnion, s, index_q, pooled, pooled_off, seq_len, slot_map, slot_off,
+                     k_cache, v_cache, q, softmax_scale, token_ids, width, out, lse, ws, ws_bytes,
+                     timer, stream);
+}
+
+int qsa_union_gather(const qsa_shape* s, const int32_t* token_ids, const int32_t* width,
+                     const int32_t* seq_len, const int32_t* slot_map, const int64_t* slot_off,
+                     const float* k_cache, const float* v_cache, float* k_union, float* v_union,
+                     int32_t* union_pos, int32_t* union_groups, void* ws, size_t ws_bytes,
+                     qsa_stream stream) {
+  int rc = validate(s, kNeedBudget | kNeedAttn);
+  if (rc != QSA_OK) return rc;
+  if (!token_ids || !width || !seq_len || !slot_map || !slot_off || !k_cache || !v_cache ||
+      !k_union || !v_union || !union_pos || !ws)
+    return QSA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_union) || !aligned16(v_union))
+    return QSA_ERR_SHAPE;
+  if (rows_per_pass(s) != row_count(s)) return QSA_ERR_UNSUPPORTED;  // one union for all rows
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
+  const UnionArgs ua = union_args(s, L, (char*)ws, token_ids, width, seq_len, slot_map, slot_off,
+                                  k_cache, v_cache, 0, row_count(s), k_union, v_union, union_pos,
+                                  union_groups);
+  return hip_status(launch_union(ua, (hipStream_t)stream));
+}
+
+int qsa_online_attend_indexed(const qsa_shape* s, const float* q, const float* k_rows,
+                              const float* v_rows, int64_t n_rows, const int32_t* row_pos,
+                              const int32_t* width, float softmax_scale, float* out, float* lse,
+                              void* ws, size_t ws_bytes, qsa_stream stream) {
+  int rc = validate(s, kNeedBudget | kNeedAttn);
+  if (rc != QSA_OK) return rc;
+  if (!q || !k_rows || !v_rows || !row_pos || !width || !out || !ws) return QSA_ERR_NULL;
+  if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(q) || !aligned16(out))
+    return QSA_ERR_SHAPE;
+  if (n_rows < 1 || n_rows > INT32_MAX) return QSA_ERR_SHAPE;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
+  const int64_t rows = row_count(s), R = rows_per_pass(s);
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t r0 = 0; r0 < rows; r0 += R) {
+    const int64_t n = (rows - r0) < R ? (rows - r0) : R;
+    AttendArgs a{q, nullptr, nullptr, width, s->q_heads, s->kv_heads, s->head_dim,
+                 token_stride(s), attn_chunks(s), softmax_scale, r0, n,
+                 reinterpret_cast<float*>((char*)ws + L.pacc),
+                 reinterpret_cast<float*>((char*)ws + L.pml), out, lse};
+    a.union_pos = row_pos + r0 * token_stride(s);
+    a.k_cache = k_rows;
+    a.v_cache = v_rows;
+    a.kv_slots = n_rows;
+    if (launch_attend(a, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_merge(a, st) != hipSuccess) return QSA_ERR_HIP;
+  }
+  return QSA_OK;
 }
 
 }  // extern "C"

@@ -66,11 +66,14 @@ __device__ __forceinline__ Item item_of(int64_t it, int64_t rows, int kv_heads) 
 // inside this kernel, two items ahead of their use, into a three-deep LDS
 // ring (wavefront 0: ID loads at the top of an item, slot-map loads after its
 // scores, LDS write at its end), so the row loads of the next item can be
-// issued as early as in the compact path.  Both produce the same bits.
+// issued as early as in the compact path.  Union: like fused, but the
+// positions are read from a per-row list into the union scratch of the chunk
+// gather (union.hip) and need no slot map.  All three produce the same bits.
+enum Mode { kCompact = 0, kFused = 1, kUnion = 2 };
 struct RowSource {
   const float* k_compact;
   const float* v_compact;
-  const int32_t* token_ids;  // fused only, global rows
+  const int32_t* token_ids;  // fused: global rows; union: positions, local rows
   const int32_t* seq_len;
   const int32_t* slot_map;
   const int64_t* slot_off;
@@ -80,13 +83,14 @@ struct RowSource {
   int32_t queries;
 };
 
-template <int D, int GQ, bool FUSED>
+template <int D, int GQ, int MODE>
 __global__ void __launch_bounds__(4 * kWave)
 attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* __restrict__ width,
                     int32_t q_heads, int32_t kv_heads, int32_t stride, int32_t n_chunks,
                     float scale, int64_t row0, int64_t rows, float* __restrict__ part_acc,
                     float* __restrict__ part_ml) {
   using A = AttnCfg<D, GQ>;
+  constexpr bool FUSED = MODE != kCompact;
   constexpr int NW = A::NW, NT = A::NT, HPW = A::HPW, KPW = A::KPW, KP = A::KP;
   constexpr int DPL = A::DPL, KV4 = A::KV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
@@ -158,14 +162,16 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   auto resolve_ids = [&](const Item& x, int cn_x) {
     if constexpr (FUSED) {
       if (wave == 0) {
-        const int64_t row = row0 + x.lrow;
+        const int64_t row = MODE == kUnion ? x.lrow : row0 + x.lrow;
         id_reg = lane < cn_x ? src.token_ids[row * stride + (int64_t)x.chunk * C + lane] : -1;
       }
     }
   };
   auto resolve_slots = [&](const Item& x, int cn_x) {
     if constexpr (FUSED) {
-      if (wave == 0) {
+      if (wave == 0 && MODE == kUnion) {
+        slot_reg = lane < cn_x ? ((id_reg >= 0 && (int64_t)id_reg < src.kv_slots) ? id_reg : -1) : 0;
+      } else if (wave == 0) {
         const int64_t row = row0 + x.lrow;
         const int32_t b = (int32_t)(row / src.queries);
         const int64_t n = (int64_t)src.seq_len[b] - src.queries + 1 + (row - (int64_t)b * src.queries);
@@ -419,9 +425,8 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
   }
 }
 
-// Persistent launch: as many workgroups as can be resident at once (queried
-// once per kernel instance), each walking the work items with a stride of the
-// grid size.
+}  // namespace
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -430,13 +435,19 @@ int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-template <int D, int GQ, bool FUSED>
+namespace {
+
+// Persistent launch: as many workgroups as can be resident at once (queried
+// once per kernel instance), each walking the work items with a stride of the
+// grid size.
+
+template <int D, int GQ, int MODE>
 hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
   using A = AttnCfg<D, GQ>;
   static int per_cu = 0;  // resident workgroups per compute unit for this instance
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ, FUSED>, A::NT,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ, MODE>, A::NT,
                                                      0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -445,9 +456,9 @@ hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
   const int64_t items = (int64_t)a.n_chunks * a.rows * a.kv_heads;
   const int64_t slots = (int64_t)device_cus() * per_cu;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
-  RowSource src{a.k_compact, a.v_compact, a.token_ids, a.seq_len, a.slot_map, a.slot_off,
-                a.k_cache, a.v_cache, a.kv_slots, a.queries};
-  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ, FUSED>), dim3(grid), dim3(A::NT), 0, s, a.q, src,
+  RowSource src{a.k_compact, a.v_compact, MODE == kUnion ? a.union_pos : a.token_ids, a.seq_len,
+                a.slot_map, a.slot_off, a.k_cache, a.v_cache, a.kv_slots, a.queries};
+  hipLaunchKernelGGL((attend_chunk_kernel<D, GQ, MODE>), dim3(grid), dim3(A::NT), 0, s, a.q, src,
                      a.width, a.q_heads, a.kv_heads, a.stride, a.n_chunks, a.scale, a.row0,
                      a.rows, a.part_acc, a.part_ml);
   return hipGetLastError();
@@ -455,7 +466,9 @@ hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
 
 template <int D, int GQ>
 hipError_t launch_attend_f(const AttendArgs& a, hipStream_t s) {
-  return a.token_ids ? launch_attend_t<D, GQ, true>(a, s) : launch_attend_t<D, GQ, false>(a, s);
+  if (a.union_pos) return launch_attend_t<D, GQ, kUnion>(a, s);
+  if (a.token_ids) return launch_attend_t<D, GQ, kFused>(a, s);
+  return launch_attend_t<D, GQ, kCompact>(a, s);
 }
 
 template <int D>

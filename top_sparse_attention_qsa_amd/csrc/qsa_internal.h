@@ -200,6 +200,38 @@ struct AttendArgs {
   const float* v_cache = nullptr;
   int64_t kv_slots = 0;
   int32_t queries = 1;
+  // union path (union_pos != null): row i of a row is k_cache/v_cache row
+  // union_pos[row][i] (< kv_slots; negative: invalid), no slot map
+  const int32_t* union_pos = nullptr;  // local rows
+};
+
+// One pass of the union gather (union.hip).
+struct UnionArgs {
+  const int32_t* token_ids;  // global rows
+  const int32_t* width;      // global rows
+  const int32_t* seq_len;
+  const int32_t* slot_map;
+  const int64_t* slot_off;
+  const float* k_cache;
+  const float* v_cache;
+  int32_t queries;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t stride;            // 4k+4
+  int64_t kv_slots;
+  int64_t max_groups;
+  int64_t row0;
+  int64_t rows;
+  int32_t cus;               // compute units (gather grid)
+  uint32_t* row_bitmap;      // [rows][union_words_per_seq]
+  uint32_t* union_bitmap;    // [union_seqs_per_pass][union_words_per_seq]
+  uint32_t* word_prefix;     // same shape as union_bitmap
+  uint32_t* block_prefix;    // [union_scan_blocks(words) + 1]
+  int2* union_list;          // [rows * (k+1)]
+  float* k_union;            // [rows * (4k+4)][H_kv][D]
+  float* v_union;
+  int32_t* union_pos;        // [rows][4k+4] local rows
+  int32_t* count_out;        // union groups, may be null
 };
 
 struct ChunkArgs {
@@ -255,5 +287,10 @@ hipError_t launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, 
 bool chunk_supported(int h_i, int queries, int64_t rows_per_launch);
 hipError_t launch_chunk(const ChunkArgs& a, int h_i, int d_i, hipStream_t s);
 hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hipStream_t s);
+int64_t union_words_per_seq(int64_t max_groups);
+int64_t union_seqs_per_pass(int64_t rows_per_pass, int32_t queries, int32_t batch);
+int64_t union_scan_blocks(int64_t words);
+hipError_t launch_union(const UnionArgs& a, hipStream_t s);
+int device_cus();
 
 }  // namespace qsa
