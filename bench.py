@@ -60,7 +60,7 @@ def fused_algorithmic_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=12
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("score.hip", "qsa_internal.h"):
+    for f in ("score.hip", "qsa_device.h"):
         with open(os.path.join(ROOT, "top_sparse_attention_qsa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

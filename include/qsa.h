@@ -57,7 +57,9 @@ extern "C" {
 #define QSA_GROUP 4          /* tokens per group ([SET] §Decision)                 */
 #define QSA_MAX_BUDGET 1024  /* largest supported k (the notes use k = 512)        */
 #define QSA_KEY_TILE 64      /* groups per pooled-key tile (layout below)          */
-#define QSA_DECODE_STAGES 5  /* kernels timed by qsa_timer in one qsa_decode call  */
+#define QSA_DECODE_STAGES 5  /* stages timed by qsa_timer in one qsa_decode call:
+                                score, select+emit, resolve+gather, attention
+                                chunks, merge of the chunk partials               */
 
 typedef void *qsa_stream; /* a hipStream_t */
 
@@ -211,8 +213,9 @@ QSA_API int qsa_online_attend(const qsa_shape *shape, const float *q, const floa
                       float *out, float *lse, void *workspace, size_t workspace_bytes,
                       qsa_stream stream);
 
-/* Stage timer for qsa_decode: HIP events recorded around each of the
- * QSA_DECODE_STAGES kernels of up to max_calls calls. */
+/* Stage timer for qsa_decode and its variants: HIP events recorded around
+ * each of the QSA_DECODE_STAGES stages of up to max_calls calls (with
+ * several passes of rows_in_flight rows, around the first pass). */
 typedef struct qsa_timer qsa_timer;
 QSA_API int qsa_timer_create(int32_t max_calls, qsa_timer **timer);
 /* Waits for the recorded calls and writes ms[call][stage] for the n calls

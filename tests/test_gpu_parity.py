@@ -234,9 +234,11 @@ def test_budgets(k):
 
 def test_all_scores_tied_streaming_path():
     """A zero index query makes every score +0: more candidates than LDS holds,
-    so the streaming path runs and must keep groups 0..k-1."""
-    spec = inputs.custom("ties", [20000, 70001, 513], h_i=4, d_i=32, h_q=1, h_kv=1, d=64,
-                         keys="zero_query")
+    so the streaming path runs and must keep groups 0..k-1 (reached through
+    each candidate pass: 1,024 segments all at the threshold, 5,000 segments
+    -- too many to list -- and the full scan)."""
+    spec = inputs.custom("ties", [20000, 70001, 513, 65536, 80000], h_i=4, d_i=32, h_q=1,
+                         h_kv=1, d=64, keys="zero_query")
     case = run_and_check(spec)
     ids = case.token_ids.cpu().numpy()
     assert np.array_equal(ids[0, :2048], np.arange(2048))

@@ -1,129 +1,11 @@
-// qsa_internal.h -- device helpers and kernel launchers shared by the HIP
-// sources of libqsa.so (gfx950, wave64).  Not part of the public ABI.
+// qsa_internal.h -- kernel argument blocks and launchers shared by the HIP
+// sources of libqsa.so.  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
 #include "qsa.h"
+#include "qsa_device.h"
 
 namespace qsa {
-
-constexpr int kWave = 64;
-constexpr int kScoreWaves = 4;        // waves (one 64-group tile each) per scoring workgroup
-constexpr int kSegment = 16;          // groups per maximum used to bound the threshold
-constexpr int kSelectThreads = 1024;  // one selection workgroup per row
-constexpr int kCandCap = 4096;        // candidates kept in LDS before the streaming path
-constexpr int kGatherTokens = 8;      // compact rows per gather workgroup
-constexpr int kAttnChunk = 64;        // compact rows per attention partial
-
-// Scores are ordered through a monotone unsigned key: -0 is folded onto +0,
-// then non-negative floats get their sign bit set and negative floats are
-// bit-inverted, so unsigned comparison equals float comparison.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-struct RowView {
-  int64_t n;     // visible tokens
-  int64_t g;     // complete groups
-  int32_t tail;  // n mod 4
-  int32_t b;     // sequence
-  bool valid;
-};
-
-__device__ __forceinline__ RowView row_view(const int32_t* __restrict__ seq_len, int64_t row,
-                                            int32_t queries, int64_t g_max) {
-  RowView v;
-  v.b = (int32_t)(row / queries);
-  const int32_t j = (int32_t)(row - (int64_t)v.b * queries);
-  v.n = (int64_t)seq_len[v.b] - queries + 1 + j;
-  v.valid = v.n >= 0;
-  v.g = v.valid ? (v.n >> 2) : 0;
-  v.tail = v.valid ? (int32_t)(v.n & 3) : 0;
-  if (v.g > g_max) v.valid = false;
-  return v;
-}
-
-__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
-
-// Index of this wavefront within its workgroup, as a value the compiler knows
-// to be uniform (so addresses derived from it use scalar loads).
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-}
-
-// Number of set bits of `mask` below this lane.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(v, o, kWave);
-    if (lane >= o) v += y;
-  }
-  return v;
-}
-
-// Wavefront reductions.  Within each 16-lane DPP row, rotations by 1, 2, 4
-// and 8 lanes (row_ror) leave every lane holding its row's reduction; lane 0
-// of each row is then read into a scalar and the four rows are combined as
-// (r0 op r1) op (r2 op r3).  The order is fixed, so a sum is the same bits on
-// every run and the result is uniform across the wavefront.  DPP stays in
-// the VALU: no LDS round trips.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
-
-__device__ __forceinline__ float read_lane(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f32<kRowRor1>(v));
-  v = fmaxf(v, dpp_f32<kRowRor2>(v));
-  v = fmaxf(v, dpp_f32<kRowRor4>(v));
-  v = fmaxf(v, dpp_f32<kRowRor8>(v));
-  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v = v + dpp_f32<kRowRor1>(v);
-  v = v + dpp_f32<kRowRor2>(v);
-  v = v + dpp_f32<kRowRor4>(v);
-  v = v + dpp_f32<kRowRor8>(v);
-  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
-}
-
-// Exclusive prefix sum over a whole workgroup of NT threads (NT/64 waves);
-// `wave_tot` is LDS scratch of NT/64 words.  *total receives the sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* wave_tot,
-                                                        uint32_t* total) {
-  constexpr int NW = NT / kWave;
-  const int wave = (int)(threadIdx.x / kWave);
-  const uint32_t inc = wave_inclusive_sum(x);
-  if (lane_id() == kWave - 1) wave_tot[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t t = wave_tot[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + inc - x;
-}
 
 // ---------------------------------------------------------------- launchers
 struct ScoreArgs {

@@ -32,6 +32,8 @@ constexpr int NWAVES = NT / kWave;
 
 constexpr int kMaxStage = 4096;   // segment maxima staged in LDS (G <= 65,536)
 constexpr int kPerThread = 32;    // scores held per thread in one streaming pass
+constexpr int kSegCap = 1024;     // segments the segment-skipping candidate pass can visit
+constexpr int kSegItems = kSegCap * kSegment / NT;  // scores per thread in that pass
 
 struct SelectShared {
   uint32_t hist[256];
@@ -62,13 +64,16 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 }
 
 // k-th largest order key among n keys from src (1 <= k <= n) and the count of
-// keys strictly above it.  Four passes of 8 bits, most significant first.
-template <class Src>
+// keys strictly above it: PASSES passes of 8 bits, most significant first.
+// With fewer than four passes the result is the k-th largest key with its
+// undecided low bits cleared -- a lower bound of it -- and the count is that
+// of keys above the decided prefix.
+template <class Src, int PASSES = 4>
 __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, SelectShared& sh,
                                   uint32_t* t_out, uint32_t* above_out) {
   const int tid = (int)threadIdx.x;
   uint32_t prefix = 0, mask = 0, kk = k, above = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = 24; shift >= 32 - 8 * PASSES; shift -= 8) {
     for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     __syncthreads();
     const uint32_t n_up = (n + NT - 1) / NT * NT;   // whole wavefronts stay converged
@@ -197,6 +202,101 @@ struct Emitter {
   }
 };
 
+// Candidate compaction that reads only the segments that can hold a member
+// (decode rows, whose scores are exact).  Each thread owns the maxima of four
+// consecutive segments in registers; tau = a lower bound of the k-th largest
+// of the (folded) maxima, from a two-pass radix select on their top 16 bits.
+// A segment whose maximum is below tau holds no group scoring >= tau, so only
+// the segments reaching tau are listed (in order) and their scores read;
+// scores >= tau are compacted in position order into LDS.  Returns false,
+// having changed nothing but LDS, when more than kSegCap segments reach tau;
+// sets *overflow when more than kCandCap candidates survive.
+__device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ srow,
+                                   const uint32_t* __restrict__ mrow, uint32_t G, uint32_t segs,
+                                   uint32_t k, uint32_t* n_cand, bool* overflow) {
+  const int tid = (int)threadIdx.x;
+  const uint32_t s0 = 4u * (uint32_t)tid;
+  uint32_t mx[4];
+  if (s0 + 4 <= segs) {
+    const uint4 v = *reinterpret_cast<const uint4*>(mrow + s0);
+    mx[0] = v.x; mx[1] = v.y; mx[2] = v.z; mx[3] = v.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx[e] = (s0 + e < segs) ? mrow[s0 + e] : 0u;
+  }
+  // fold f neighbouring maxima into one while at least 2k values remain; each
+  // folded value is still the maximum of a disjoint set of groups
+  uint32_t f = 1;
+  while (f < 4 && (segs / (2 * f)) >= 2u * k) f *= 2;
+  const uint32_t nf = (segs + f - 1) / f;
+  if (f == 4) {
+    const uint32_t a = mx[0] > mx[1] ? mx[0] : mx[1], b = mx[2] > mx[3] ? mx[2] : mx[3];
+    if (s0 / 4 < nf) sh.maxima[s0 / 4] = a > b ? a : b;
+  } else if (f == 2) {
+    if (s0 / 2 < nf) sh.maxima[s0 / 2] = mx[0] > mx[1] ? mx[0] : mx[1];
+    if (s0 / 2 + 1 < nf) sh.maxima[s0 / 2 + 1] = mx[2] > mx[3] ? mx[2] : mx[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s0 + e < nf) sh.maxima[s0 + e] = mx[e];
+  }
+  __syncthreads();
+  uint32_t tau, above_unused;
+  radix_kth_largest<LdsCands, 2>(LdsCands{sh.maxima}, nf, k, sh, &tau, &above_unused);
+
+  // list the segments that reach tau, in order (the list reuses sh.maxima)
+  uint32_t fl = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (s0 + e < segs && mx[e] >= tau) fl |= 1u << e;
+  uint32_t nseg;
+  uint32_t o = block_exclusive_sum<NT>((uint32_t)__popc(fl), sh.wave_tot, &nseg);
+  if (nseg > (uint32_t)kSegCap) return false;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((fl >> e) & 1u) sh.maxima[o++] = s0 + e;
+  __syncthreads();
+
+  // their scores: thread t reads list items [t*J, (t+1)*J), item i being
+  // group 16*list[i/16] + i%16, so the items are in position order
+  const uint32_t items = nseg * kSegment;
+  const uint32_t J = (items + NT - 1) / NT;  // <= kSegItems
+  uint32_t key[kSegItems];
+  uint32_t cf = 0;
+#pragma unroll
+  for (int j = 0; j < kSegItems; ++j) {
+    const uint32_t i = (uint32_t)tid * J + j;
+    key[j] = 0u;
+    if ((uint32_t)j < J && i < items) {
+      const uint32_t p = sh.maxima[i / kSegment] * kSegment + (i % kSegment);
+      if (p < G) key[j] = order_key(srow[p]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSegItems; ++j) {
+    const uint32_t i = (uint32_t)tid * J + j;
+    if ((uint32_t)j < J && i < items && key[j] >= tau &&
+        sh.maxima[i / kSegment] * kSegment + (i % kSegment) < G)
+      cf |= 1u << j;
+  }
+  uint32_t tot;
+  uint32_t c = block_exclusive_sum<NT>((uint32_t)__popc(cf), sh.wave_tot, &tot);
+  if (tot > (uint32_t)kCandCap) {
+    *overflow = true;
+    return true;
+  }
+#pragma unroll
+  for (int j = 0; j < kSegItems; ++j)
+    if ((cf >> j) & 1u) {
+      const uint32_t i = (uint32_t)tid * J + j;
+      sh.cand_key[c] = key[j];
+      sh.cand_pos[c] = sh.maxima[i / kSegment] * kSegment + (i % kSegment);
+      ++c;
+    }
+  *n_cand = tot;
+  return true;
+}
+
 template <class P>
 __device__ void select_row(const P& pol, SelectShared& sh, const float* __restrict__ scores,
                            const uint32_t* __restrict__ maxima, const RowView& rv, int64_t lrow,
@@ -229,13 +329,22 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     kept = G;
   } else {
     const float* __restrict__ srow = scores + lrow * g_max;
+    uint32_t n_cand = 0;
+    bool overflow = false;
+    bool compacted = false;  // candidates already in LDS (segment-skipping pass)
+    const uint32_t segs = (G + kSegment - 1) / kSegment;
+    if constexpr (!P::kCertified) {
+      if (maxima && segs >= (uint32_t)k && segs <= 4u * NT)
+        compacted = segment_candidates(sh, srow, maxima + lrow * (g_max / kSegment), G, segs,
+                                       (uint32_t)k, &n_cand, &overflow);
+    }
+    if (!compacted) {
     // 1. threshold bound from the segment maxima, staged once in LDS.  While
     //    at least 2k would remain, f neighbouring maxima are folded into one
     //    (their maximum): still one maximum per disjoint set of groups, so the
     //    k-th largest of the folded values is still a lower bound of the k-th
     //    largest score, and the radix select works on fewer values.
     uint32_t tau = 0;
-    const uint32_t segs = (G + kSegment - 1) / kSegment;
     if (maxima && segs >= (uint32_t)k) {
       const uint32_t* mrow = maxima + lrow * (g_max / kSegment);
       uint32_t f = 1;
@@ -265,8 +374,6 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     //    output index is the workgroup prefix of the wavefront totals, plus the
     //    wavefront's running count over j, plus a bit-sliced ballot prefix over
     //    the lanes below it.
-    uint32_t n_cand = 0;
-    bool overflow = false;
     constexpr int NJ = kPerThread / 4;
     const int lane = lane_id();
     const int wave = wave_id();
@@ -328,6 +435,7 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
       }
       n_cand += tot;
     }
+    }  // !compacted
     __syncthreads();
     if constexpr (P::kCertified) {
       // the candidates' bounds are replaced by their exact (chain) keys
