@@ -213,13 +213,17 @@ QSA_API int qsa_online_attend(const qsa_shape *shape, const float *q, const floa
                       float *out, float *lse, void *workspace, size_t workspace_bytes,
                       qsa_stream stream);
 
-/* Stage timer for qsa_decode and its variants: HIP events recorded around
- * each of the QSA_DECODE_STAGES stages of up to max_calls calls (with
- * several passes of rows_in_flight rows, around the first pass). */
+/* Stage timer for qsa_decode and its variants: HIP events recorded on the
+ * call's stream around the stages in stage_mask (bit s = stage s, nonzero,
+ * below 1 << QSA_DECODE_STAGES) of up to max_calls calls; with several
+ * passes of rows_in_flight rows, around the first pass.  Each recorded event
+ * costs the stream a few microseconds, so time only the stages needed. */
+#define QSA_TIMER_ALL ((1u << QSA_DECODE_STAGES) - 1u)
 typedef struct qsa_timer qsa_timer;
-QSA_API int qsa_timer_create(int32_t max_calls, qsa_timer **timer);
+QSA_API int qsa_timer_create(int32_t max_calls, uint32_t stage_mask, qsa_timer **timer);
 /* Waits for the recorded calls and writes ms[call][stage] for the n calls
- * made since creation or the last reset (n returned in *calls). */
+ * made since creation or the last reset (n returned in *calls); stages not
+ * in the mask read -1. */
 QSA_API int qsa_timer_read(qsa_timer *timer, float *ms_host, int32_t *calls_host);
 QSA_API void qsa_timer_reset(qsa_timer *timer);
 QSA_API void qsa_timer_destroy(qsa_timer *timer);

@@ -127,7 +127,10 @@ def test_null_pointers_and_small_workspace_rejected():
     odd = ctypes.c_void_p(258)
     assert L.qsa_score_groups(ctypes.byref(s), p, odd, p, p, p, None) == qsa.QSA_ERR_SHAPE
     assert L.qsa_accounting(ctypes.byref(s), 10, None) == qsa.QSA_ERR_NULL
-    assert L.qsa_timer_create(0, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_timer_create(0, 1, None) == qsa.QSA_ERR_NULL
+    h = ctypes.c_void_p()
+    assert L.qsa_timer_create(4, 0, ctypes.byref(h)) == qsa.QSA_ERR_SHAPE  # no stage
+    assert L.qsa_timer_create(4, 1 << qsa.DECODE_STAGES, ctypes.byref(h)) == qsa.QSA_ERR_SHAPE
 
 
 def test_binding_refuses_host_tensors():

@@ -91,7 +91,7 @@ def lib():
             "qsa_emit_chronological": ([S, P, P, P, P, P], ctypes.c_int),
             "qsa_resolve_gather": ([S, P, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "qsa_online_attend": ([S, P, P, P, P, f32, P, P, P, sz, P], ctypes.c_int),
-            "qsa_timer_create": ([i32, ctypes.POINTER(P)], ctypes.c_int),
+            "qsa_timer_create": ([i32, ctypes.c_uint32, ctypes.POINTER(P)], ctypes.c_int),
             "qsa_timer_read": ([P, P, ctypes.POINTER(i32)], ctypes.c_int),
             "qsa_timer_reset": ([P], None),
             "qsa_timer_destroy": ([P], None),
@@ -306,9 +306,12 @@ def qsa_accounting(shape, total_tokens):
 class Timer:
     """qsa_timer: HIP events around each qsa_decode stage."""
 
-    def __init__(self, max_calls):
+    def __init__(self, max_calls, stages=None):
+        """stages: names from STAGE_NAMES to time (default: all)."""
+        mask = (1 << DECODE_STAGES) - 1 if stages is None else \
+            sum(1 << STAGE_NAMES.index(n) for n in stages)
         h = ctypes.c_void_p()
-        _check(lib().qsa_timer_create(int(max_calls), ctypes.byref(h)), "qsa_timer_create")
+        _check(lib().qsa_timer_create(int(max_calls), mask, ctypes.byref(h)), "qsa_timer_create")
         self.handle = h
         self.max_calls = int(max_calls)
 

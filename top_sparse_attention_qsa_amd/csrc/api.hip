@@ -114,6 +114,7 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_
 struct qsa_timer {
   int32_t max_calls;
   int32_t calls;
+  uint32_t mask;   // stages timed (bit s: stage s)
   hipEvent_t* ev;  // [max_calls][QSA_DECODE_STAGES + 1]
 };
 
@@ -272,15 +273,17 @@ int qsa_online_attend(const qsa_shape* s, const float* q, const float* k_compact
   return QSA_OK;
 }
 
-int qsa_timer_create(int32_t max_calls, qsa_timer** timer) {
+int qsa_timer_create(int32_t max_calls, uint32_t stage_mask, qsa_timer** timer) {
   if (!timer) return QSA_ERR_NULL;
   if (max_calls < 1 || max_calls > (1 << 20)) return QSA_ERR_SHAPE;
+  if (stage_mask == 0 || (stage_mask >> QSA_DECODE_STAGES) != 0) return QSA_ERR_SHAPE;
   qsa_timer* t = new (std::nothrow) qsa_timer;
   if (!t) return QSA_ERR_HIP;
   const int32_t n = max_calls * (QSA_DECODE_STAGES + 1);
   t->ev = new (std::nothrow) hipEvent_t[n];
   t->max_calls = max_calls;
   t->calls = 0;
+  t->mask = stage_mask;
   if (!t->ev) {
     delete t;
     return QSA_ERR_HIP;
@@ -301,10 +304,14 @@ int qsa_timer_read(qsa_timer* t, float* ms, int32_t* calls) {
   if (!t || !ms || !calls) return QSA_ERR_NULL;
   for (int32_t c = 0; c < t->calls; ++c) {
     hipEvent_t* e = t->ev + (size_t)c * (QSA_DECODE_STAGES + 1);
-    if (hipEventSynchronize(e[QSA_DECODE_STAGES]) != hipSuccess) return QSA_ERR_HIP;
+    int last = QSA_DECODE_STAGES;  // the last event recorded for this call
+    while (last > 0 && !((t->mask >> (last - 1)) & 1u)) --last;
+    if (hipEventSynchronize(e[last]) != hipSuccess) return QSA_ERR_HIP;
     for (int st = 0; st < QSA_DECODE_STAGES; ++st) {
-      float v = 0.f;
-      if (hipEventElapsedTime(&v, e[st], e[st + 1]) != hipSuccess) return QSA_ERR_HIP;
+      float v = -1.0f;  // stage not timed
+      if ((t->mask >> st) & 1u) {
+        if (hipEventElapsedTime(&v, e[st], e[st + 1]) != hipSuccess) return QSA_ERR_HIP;
+      }
       ms[(size_t)c * QSA_DECODE_STAGES + st] = v;
     }
   }
@@ -398,7 +405,15 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
     const int64_t n = (rows - r0) < R ? (rows - r0) : R;
     const bool timed = ev && r0 == 0;  // with several passes the events bracket the first
-    if (timed && hipEventRecord(ev[0], st) != hipSuccess) return QSA_ERR_HIP;
+    // event i opens stage i and closes stage i-1; only those of timed stages
+    // are recorded, so an untimed stage adds nothing to the stream
+    auto record = [&](int i) -> bool {
+      if (!timed) return true;
+      const uint32_t m = timer->mask;
+      const bool need = ((m >> i) & 1u) || (i > 0 && ((m >> (i - 1)) & 1u));
+      return !need || hipEventRecord(ev[i], st) == hipSuccess;
+    };
+    if (!record(0)) return QSA_ERR_HIP;
     if (chunk) {
       ChunkArgs ca{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
                    nullptr, nullptr, scores, maxima};
@@ -408,7 +423,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
                    scores, maxima};
       if (launch_score(sa, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
     }
-    if (timed && hipEventRecord(ev[1], st) != hipSuccess) return QSA_ERR_HIP;
+    if (!record(1)) return QSA_ERR_HIP;
     SelectArgs se{scores, maxima, seq_len, s->queries, s->max_groups, s->budget_groups,
                   r0, n, nullptr, token_ids, width};
     if (chunk) {
@@ -417,7 +432,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
     } else if (launch_select(se, st) != hipSuccess) {
       return QSA_ERR_HIP;
     }
-    if (timed && hipEventRecord(ev[2], st) != hipSuccess) return QSA_ERR_HIP;
+    if (!record(2)) return QSA_ERR_HIP;
     int32_t* upos = reinterpret_cast<int32_t*>(w + L.upos);
     if (mode == Rows::kCompact) {
       GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
@@ -429,7 +444,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
                                       k_cache, v_cache, r0, n, kc, vc, upos, nullptr);
       if (launch_union(ua, st) != hipSuccess) return QSA_ERR_HIP;
     }
-    if (timed && hipEventRecord(ev[3], st) != hipSuccess) return QSA_ERR_HIP;
+    if (!record(3)) return QSA_ERR_HIP;
     AttendArgs aa{q, kc, vc, width, s->q_heads, s->kv_heads, s->head_dim, token_stride(s),
                   attn_chunks(s), softmax_scale, r0, n, pacc, pml, out, lse};
     if (mode == Rows::kUnion) {
@@ -448,9 +463,9 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
       aa.queries = s->queries;
     }
     if (launch_attend(aa, st) != hipSuccess) return QSA_ERR_HIP;
-    if (timed && hipEventRecord(ev[4], st) != hipSuccess) return QSA_ERR_HIP;
+    if (!record(4)) return QSA_ERR_HIP;
     if (launch_merge(aa, st) != hipSuccess) return QSA_ERR_HIP;
-    if (timed && hipEventRecord(ev[5], st) != hipSuccess) return QSA_ERR_HIP;
+    if (!record(5)) return QSA_ERR_HIP;
   }
   if (timer) timer->calls += 1;
   return QSA_OK;

@@ -348,13 +348,19 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 // Merge of the chunk partials of one (query head, row): lane c holds chunk
 // c's (m_c, l_c) and its weight a_c = exp(m_c - m); four wavefronts each fold
 // a contiguous quarter of the chunks in ascending order (weights broadcast
-// from their lanes), then the quarters are added in order.
+// from their lanes), then the quarters are added in order.  Every load a
+// wavefront needs -- all (m_c, l_c) and its quarter's accumulators -- is
+// issued before the first use, so the merge costs one memory round trip.
+constexpr int kMaxChunks = (4 * QSA_MAX_BUDGET + 3 + C - 1) / C;  // 65
+constexpr int kMaxQuarter = (kMaxChunks + 3) / 4;                  // 17
+
 template <int D>
 __global__ void __launch_bounds__(4 * kWave)
 merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_ml,
              const int32_t* __restrict__ width, int32_t q_heads, int32_t n_chunks,
              int32_t stride, int64_t row0, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int DPL = D / kWave;
+  static_assert(kMaxChunks <= 2 * kWave, "two chunk batches per lane at most");
   __shared__ float red[4][D + 1];
   const int wave = wave_id();
   const int lane = lane_id();
@@ -374,34 +380,41 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
   }
   const int nc = (w + C - 1) / C;
   const int64_t base = (lrow * q_heads + hq) * n_chunks;
-  // the running maximum over all chunks (every wavefront computes it)
-  float mx = -INFINITY;
-  for (int c = lane; c < nc; c += kWave) mx = fmaxf(mx, part_ml[(base + c) * 2]);
-  const float m = wave_max(mx);
   const int per = (nc + 3) / 4;
   const int cb = wave * per;
-  const int ce = (cb + per) < nc ? (cb + per) : nc;
+  const int cnt = (cb + per) < nc ? per : (nc > cb ? nc - cb : 0);
+  // loads: (m, l) of chunks lane and lane + 64; this quarter's accumulators
+  // (indexes are clamped to chunk nc-1, so every load is in bounds)
+  const int c0 = lane < nc ? lane : nc - 1;
+  const int c1 = lane + kWave < nc ? lane + kWave : nc - 1;
+  float2 ml0 = *reinterpret_cast<const float2*>(part_ml + (base + c0) * 2);
+  float2 ml1 = *reinterpret_cast<const float2*>(part_ml + (base + c1) * 2);
+  if (lane >= nc) ml0 = make_float2(-INFINITY, 0.0f);
+  if (lane + kWave >= nc) ml1 = make_float2(-INFINITY, 0.0f);
+  float pa[kMaxQuarter][DPL];
+#pragma unroll
+  for (int t = 0; t < kMaxQuarter; ++t) {
+    const int c = t < cnt ? cb + t : nc - 1;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) pa[t][j] = part_acc[(base + c) * D + lane * DPL + j];
+  }
+  const float m = wave_max(fmaxf(ml0.x, ml1.x));
+  // weights: lane holds chunk lane (a0) and chunk lane + 64 (a1)
+  const float a0 = lane < nc ? expf(ml0.x - m) : 0.0f;
+  const float a1 = lane + kWave < nc ? expf(ml1.x - m) : 0.0f;
+  const float wl0 = ml0.y * a0, wl1 = ml1.y * a1;
   float l = 0.0f;
   float acc[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
-  for (int c0 = cb; c0 < ce; c0 += kWave) {
-    // lane t of this batch holds chunk c0+t's weight and weighted denominator
-    const int cl = c0 + lane;
-    float a_l = 0.0f, wl_l = 0.0f;
-    if (cl < ce) {
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + (base + cl) * 2);
-      a_l = expf(ml.x - m);
-      wl_l = ml.y * a_l;
-    }
-    const int cnt = (ce - c0) < kWave ? (ce - c0) : kWave;
-#pragma unroll 8
-    for (int t = 0; t < cnt; ++t) {
-      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_l), t));
-      l = l + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl_l), t));
-      const float* pa = part_acc + (base + c0 + t) * D + lane * DPL;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[j] = __builtin_fmaf(pa[j], a, acc[j]);
+  for (int t = 0; t < kMaxQuarter; ++t) {
+    if (t < cnt) {  // uniform
+      const int c = cb + t;
+      const float a = c < kWave ? read_lane(a0, c) : read_lane(a1, c - kWave);
+      l = l + (c < kWave ? read_lane(wl0, c) : read_lane(wl1, c - kWave));
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j] = __builtin_fmaf(pa[t][j], a, acc[j]);
     }
   }
 #pragma unroll
