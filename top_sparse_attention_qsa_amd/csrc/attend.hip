@@ -60,6 +60,27 @@ __device__ __forceinline__ Item item_of(int64_t it, int64_t rows, int kv_heads) 
   return x;
 }
 
+// Stepping a workgroup's item by the grid size adds the grid size's own
+// (chunk, row, head) digits with carries, so the item loop does no 64-bit
+// division (which the compiler expands to over a hundred scalar
+// instructions).  Digits past the last chunk are only used behind `it < items`.
+__device__ __forceinline__ Item item_step(Item x, const Item& step, int64_t rows, int kv_heads) {
+  x.hk += step.hk;
+  int64_t carry = 0;
+  if (x.hk >= kv_heads) {
+    x.hk -= kv_heads;
+    carry = 1;
+  }
+  x.lrow += step.lrow + carry;
+  int carry2 = 0;
+  if (x.lrow >= rows) {
+    x.lrow -= rows;
+    carry2 = 1;
+  }
+  x.chunk += step.chunk + carry2;
+  return x;
+}
+
 // Where a work item's K and V rows come from.  Compact: the scratch written
 // by the gather (row i of the row's compact copy).  Fused: straight from the
 // K/V cache; the chunk's logical IDs are resolved through the slot map once,
@@ -172,9 +193,9 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       if (wave == 0 && MODE == kUnion) {
         slot_reg = lane < cn_x ? ((id_reg >= 0 && (int64_t)id_reg < src.kv_slots) ? id_reg : -1) : 0;
       } else if (wave == 0) {
-        const int64_t row = row0 + x.lrow;
-        const int32_t b = (int32_t)(row / src.queries);
-        const int64_t n = (int64_t)src.seq_len[b] - src.queries + 1 + (row - (int64_t)b * src.queries);
+        const int32_t row = (int32_t)(row0 + x.lrow);  // rows fit in 32 bits (validated)
+        const int32_t b = row / src.queries;
+        const int64_t n = (int64_t)src.seq_len[b] - src.queries + 1 + (row - b * src.queries);
         slot_reg = lane < cn_x ? -1 : 0;
         if (lane < cn_x && id_reg >= 0 && (int64_t)id_reg < n) {
           const int32_t sl = src.slot_map[src.slot_off[b] + id_reg];
@@ -191,13 +212,20 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 
   int64_t it = blockIdx.x;
   int j = 0;  // this workgroup's item sequence number
-  auto item_at = [&](int64_t i) { return item_of(i < items ? i : items - 1, rows, kv_heads); };
+  // raw digits of items it, it+grid, it+2*grid; past the end, the last item
+  // (whose rows always exist) stands in for address computations
+  const Item step = item_of(gridDim.x, rows, kv_heads);
+  const Item last = item_of(items - 1, rows, kv_heads);
+  Item raw0 = item_of(it, rows, kv_heads);
+  Item raw1 = item_step(raw0, step, rows, kv_heads);
+  Item raw2 = item_step(raw1, step, rows, kv_heads);
+  auto item_at = [&](int64_t i, const Item& raw) { return i < items ? raw : last; };
   auto rows_at = [&](int64_t i, const Item& x) { return i < items ? chunk_rows(x) : 0; };
-  Item cur = item_at(it);
+  Item cur = item_at(it, raw0);
   int cn = rows_at(it, cur);
   if constexpr (FUSED) {
     // items 0 and 1 of this workgroup are resolved up front
-    const Item x1 = item_at(it + gridDim.x);
+    const Item x1 = item_at(it + gridDim.x, raw1);
     resolve_ids(cur, cn);
     resolve_slots(cur, cn);
     resolve_store(0);
@@ -211,9 +239,9 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   while (it < items) {
     const int64_t it_next = it + gridDim.x;
     const int64_t it_next2 = it_next + gridDim.x;
-    const Item nxt = item_at(it_next);
+    const Item nxt = item_at(it_next, raw1);
     const int cn_next = rows_at(it_next, nxt);
-    const Item nxt2 = item_at(it_next2);
+    const Item nxt2 = item_at(it_next2, raw2);
     const int cn_next2 = rows_at(it_next2, nxt2);
     const int rs_cur = FUSED ? j % 3 : 0, rs_next = FUSED ? (j + 1) % 3 : 0;
     // An item with no rows (cn == 0) runs the same code on masked rows and
@@ -339,6 +367,8 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       resolve_store(FUSED ? (j + 2) % 3 : 0);  // visible after the next item's first barrier
     }
     it = it_next;
+    raw1 = raw2;
+    raw2 = item_step(raw2, step, rows, kv_heads);
     cur = nxt;
     cn = cn_next;
     ++j;
