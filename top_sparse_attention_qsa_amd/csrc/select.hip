@@ -32,8 +32,6 @@ constexpr int NWAVES = NT / kWave;
 
 constexpr int kMaxStage = 4096;   // segment maxima staged in LDS (G <= 65,536)
 constexpr int kPerThread = 32;    // scores held per thread in one streaming pass
-constexpr int kSegCap = 1024;     // segments the segment-skipping candidate pass can visit
-constexpr int kSegItems = kSegCap * kSegment / NT;  // scores per thread in that pass
 
 struct SelectShared {
   uint32_t hist[256];
@@ -206,15 +204,22 @@ struct Emitter {
 // (decode rows, whose scores are exact).  Each thread owns the maxima of four
 // consecutive segments in registers; tau = a lower bound of the k-th largest
 // of the (folded) maxima, from a two-pass radix select on their top 16 bits.
-// A segment whose maximum is below tau holds no group scoring >= tau, so only
-// the segments reaching tau are listed (in order) and their scores read;
-// scores >= tau are compacted in position order into LDS.  Returns false,
-// having changed nothing but LDS, when more than kSegCap segments reach tau;
-// sets *overflow when more than kCandCap candidates survive.
+// A segment whose maximum is below tau holds no group scoring >= tau, so each
+// wavefront lists, in order, the segments of its span (256 segments) that
+// reach tau and reads only their scores, 64 at a time (four segments per
+// load instruction).  Scores >= tau are compacted in position order into LDS:
+// wavefront order, then round order, then lane order, which is position
+// order.  Returns false, having changed nothing but LDS, when a wavefront
+// lists more than kSegRounds*4 segments; sets *overflow when more than
+// kCandCap candidates survive.
+constexpr int kSegRounds = 16;  // 64-score rounds per wavefront in one pass
+
 __device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ srow,
                                    const uint32_t* __restrict__ mrow, uint32_t G, uint32_t segs,
                                    uint32_t k, uint32_t* n_cand, bool* overflow) {
   const int tid = (int)threadIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
   const uint32_t s0 = 4u * (uint32_t)tid;
   uint32_t mx[4];
   if (s0 + 4 <= segs) {
@@ -244,55 +249,68 @@ __device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ s
   uint32_t tau, above_unused;
   radix_kth_largest<LdsCands, 2>(LdsCands{sh.maxima}, nf, k, sh, &tau, &above_unused);
 
-  // list the segments that reach tau, in order (the list reuses sh.maxima)
+  // this wavefront's list of segments reaching tau (in sh.maxima, 256 per
+  // wavefront, after the radix select is done with it)
   uint32_t fl = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     if (s0 + e < segs && mx[e] >= tau) fl |= 1u << e;
-  uint32_t nseg;
-  uint32_t o = block_exclusive_sum<NT>((uint32_t)__popc(fl), sh.wave_tot, &nseg);
-  if (nseg > (uint32_t)kSegCap) return false;
+  const uint32_t c = (uint32_t)__popc(fl);
+  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+  uint32_t o = lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
+  const uint32_t nseg = (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+  uint32_t* wlist = sh.maxima + 256 * wave;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if ((fl >> e) & 1u) sh.maxima[o++] = s0 + e;
-  __syncthreads();
+    if ((fl >> e) & 1u) wlist[o++] = s0 + e;
+  // (the list is written and read by this wavefront only)
 
-  // their scores: thread t reads list items [t*J, (t+1)*J), item i being
-  // group 16*list[i/16] + i%16, so the items are in position order
+  // rounds of 64 scores: item i = 64r + lane is score i%16 of listed segment i/16
   const uint32_t items = nseg * kSegment;
-  const uint32_t J = (items + NT - 1) / NT;  // <= kSegItems
-  uint32_t key[kSegItems];
-  uint32_t cf = 0;
+  uint32_t key[kSegRounds], pos[kSegRounds];
+  uint64_t hit[kSegRounds];
+  uint32_t cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kSegItems; ++j) {
-    const uint32_t i = (uint32_t)tid * J + j;
-    key[j] = 0u;
-    if ((uint32_t)j < J && i < items) {
-      const uint32_t p = sh.maxima[i / kSegment] * kSegment + (i % kSegment);
-      if (p < G) key[j] = order_key(srow[p]);
-    }
+  for (int r = 0; r < kSegRounds; ++r) {
+    const uint32_t i = 64u * r + (uint32_t)lane;
+    const bool in = i < items;
+    const uint32_t sg = wlist[in ? i / kSegment : 0];
+    pos[r] = sg * kSegment + (i % kSegment);
+    key[r] = (in && pos[r] < G) ? order_key(srow[pos[r]]) : 0u;
   }
 #pragma unroll
-  for (int j = 0; j < kSegItems; ++j) {
-    const uint32_t i = (uint32_t)tid * J + j;
-    if ((uint32_t)j < J && i < items && key[j] >= tau &&
-        sh.maxima[i / kSegment] * kSegment + (i % kSegment) < G)
-      cf |= 1u << j;
+  for (int r = 0; r < kSegRounds; ++r) {
+    const uint32_t i = 64u * r + (uint32_t)lane;
+    hit[r] = __ballot(i < items && pos[r] < G && key[r] >= tau);
+    cnt += (uint32_t)__popcll(hit[r]);
   }
-  uint32_t tot;
-  uint32_t c = block_exclusive_sum<NT>((uint32_t)__popc(cf), sh.wave_tot, &tot);
+  const bool too_many = items > 64u * kSegRounds;
+  if (lane == 0) sh.wave_tot[wave] = too_many ? 0xFFFFFFFFu : cnt;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  bool any_too_many = false;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const uint32_t t = sh.wave_tot[w];
+    any_too_many |= t == 0xFFFFFFFFu;
+    base += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();  // wave_tot is reused by later scans
+  if (any_too_many) return false;
   if (tot > (uint32_t)kCandCap) {
     *overflow = true;
     return true;
   }
 #pragma unroll
-  for (int j = 0; j < kSegItems; ++j)
-    if ((cf >> j) & 1u) {
-      const uint32_t i = (uint32_t)tid * J + j;
-      sh.cand_key[c] = key[j];
-      sh.cand_pos[c] = sh.maxima[i / kSegment] * kSegment + (i % kSegment);
-      ++c;
+  for (int r = 0; r < kSegRounds; ++r) {
+    if ((hit[r] >> lane) & 1ull) {
+      const uint32_t at = base + lanes_below(hit[r]);
+      sh.cand_key[at] = key[r];
+      sh.cand_pos[at] = pos[r];
     }
+    base += (uint32_t)__popcll(hit[r]);
+  }
   *n_cand = tot;
   return true;
 }
@@ -480,23 +498,25 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
           gt_flags |= (key[e] > T ? 1u : 0u) << e;
         }
       }
-      uint32_t eq_tot;
-      uint32_t eq_rank = eq_base + block_exclusive_sum<NT>((uint32_t)__popc(eq_flags),
-                                                           sh.wave_tot, &eq_tot);
-      uint32_t keep_flags = gt_flags;
+      // one scan of both counts (equal in the high half, above in the low
+      // half; a round holds at most 4*NT entries, so neither half overflows)
+      uint32_t both_tot;
+      const uint32_t both = block_exclusive_sum<NT>(
+          ((uint32_t)__popc(eq_flags) << 16) | (uint32_t)__popc(gt_flags), sh.wave_tot, &both_tot);
+      const uint32_t eq_before = both >> 16, gt_before = both & 0xFFFFu;
+      const uint32_t eq_tot = both_tot >> 16, gt_tot = both_tot & 0xFFFFu;
+      // equal keys still to keep in this round, lowest positions first
+      const uint32_t rem = need > eq_base ? need - eq_base : 0u;
+      uint32_t eq_rank = eq_before;
+      uint32_t o = out_base + gt_before + (eq_before < rem ? eq_before : rem);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((eq_flags >> e) & 1u) {
-          if (eq_rank < need) keep_flags |= 1u << e;
-          ++eq_rank;
-        }
-      uint32_t keep_tot;
-      uint32_t o = out_base + block_exclusive_sum<NT>((uint32_t)__popc(keep_flags),
-                                                      sh.wave_tot, &keep_tot);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((keep_flags >> e) & 1u) em.keep(o++, pos[e]);
-      out_base += keep_tot;
+      for (int e = 0; e < 4; ++e) {
+        const bool eq = (eq_flags >> e) & 1u;
+        const bool keep = ((gt_flags >> e) & 1u) || (eq && eq_rank < rem);
+        eq_rank += eq ? 1u : 0u;
+        if (keep) em.keep(o++, pos[e]);
+      }
+      out_base += gt_tot + (eq_tot < rem ? eq_tot : rem);
       eq_base += eq_tot;
     }
     kept = out_base;  // == k
