@@ -137,7 +137,7 @@ def chunk_leg(seed, steps):
     import numpy as np
     import torch
     from tests import harness, inputs
-    spec = inputs.spec("c5", seed=seed)
+    spec = inputs.spec("chunk_8x256", seed=seed)
     data = inputs.make(spec, seed=seed, device="cuda")
     case = harness.GpuCase(data, rows_in_flight=256)
     rows = spec.rows
@@ -219,7 +219,7 @@ def main():
         copy_calibration()
         return
 
-    spec = inputs.spec("c4")
+    spec = inputs.spec("decode_32x262144")
     print(f"[bench] generating {spec.name} on cuda:0 (seed {args.seed})", file=sys.stderr,
           flush=True)
     data = inputs.make(spec, seed=args.seed, device="cuda")

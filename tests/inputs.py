@@ -51,23 +51,30 @@ class Spec:
 
 
 def spec(name: str, seed: int = 1) -> Spec:
-    """The five named workloads (sizes in the module docstring)."""
-    if name == "c1":
-        return Spec("c1", [2055], h_i=4, d_i=32, h_q=1, h_kv=1, d=64, keys="grid",
+    """The five named workloads:
+      tail_2055         one row of 2,055 tokens (513 groups + 3 tail), grid keys
+      ring_65537        one row of 65,537 tokens, ring slot map of capacity 70,000
+      dup_100000        one row of 100,000 tokens, 20% duplicated groups (ties)
+      decode_32x262144  decode batch of 32 rows of 262,144 tokens, shared
+                        8,388,608-slot cache
+      chunk_8x256       8 sequences of 2,051..262,144 tokens, 256 causal queries
+    """
+    if name == "tail_2055":
+        return Spec("tail_2055", [2055], h_i=4, d_i=32, h_q=1, h_kv=1, d=64, keys="grid",
                     slots="identity")
-    if name == "c2":
-        return Spec("c2", [65537], h_i=8, d_i=64, h_q=1, h_kv=1, d=128, keys="normal",
+    if name == "ring_65537":
+        return Spec("ring_65537", [65537], h_i=8, d_i=64, h_q=1, h_kv=1, d=128, keys="normal",
                     slots="ring", capacity=70000)
-    if name == "c3":
-        return Spec("c3", [100000], h_i=8, d_i=64, h_q=8, h_kv=1, d=128, keys="grid_dup",
+    if name == "dup_100000":
+        return Spec("dup_100000", [100000], h_i=8, d_i=64, h_q=8, h_kv=1, d=128, keys="grid_dup",
                     slots="perm")
-    if name == "c4":
-        return Spec("c4", [262144] * 32, h_i=16, d_i=128, h_q=32, h_kv=4, d=128,
+    if name == "decode_32x262144":
+        return Spec("decode_32x262144", [262144] * 32, h_i=16, d_i=128, h_q=32, h_kv=4, d=128,
                     keys="normal", slots="shared_perm")
-    if name == "c5":
+    if name == "chunk_8x256":
         g = torch.Generator().manual_seed(1000 + seed)
         lens = torch.randint(2051, 262145, (8,), generator=g).tolist()
-        return Spec("c5", lens, queries=256, h_i=16, d_i=128, h_q=32, h_kv=4, d=128,
+        return Spec("chunk_8x256", lens, queries=256, h_i=16, d_i=128, h_q=32, h_kv=4, d=128,
                     keys="normal", slots="identity")
     raise KeyError(name)
 

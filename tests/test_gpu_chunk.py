@@ -118,12 +118,12 @@ def test_chunk_all_tied_streaming_path():
     assert np.array_equal(case.token_ids[0, :2048].cpu().numpy(), np.arange(2048))
 
 
-def test_c5_chunk_equals_256_single_query_decodes():
+def test_full_chunk_equals_256_single_query_decodes():
     """8 sequences of lengths drawn from [2,051, 262,144] (plus the 2,051
     boundary), 256 causal queries each, indexer 16 x 128, attention 32 q /
     4 KV x 128: chunk results, with per-row compact gathers and with one
     union gather per sequence, equal 256 sequential decodes per sequence."""
-    spec = inputs.spec("c5", seed=1)
+    spec = inputs.spec("chunk_8x256", seed=1)
     spec.seq_lens[0] = 2051 + 255          # first row sees exactly 2,051 tokens
     data = inputs.make(spec, seed=1, device="cuda")
     case = harness.GpuCase(data, rows_in_flight=256)

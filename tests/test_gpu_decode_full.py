@@ -18,22 +18,22 @@ SAMPLED_ROWS = (0, 13, 31)
 
 
 @pytest.fixture(scope="module")
-def c4():
-    data = inputs.make(inputs.spec("c4"), seed=2, device="cuda")
+def full():
+    data = inputs.make(inputs.spec("decode_32x262144"), seed=2, device="cuda")
     case = harness.GpuCase(data)
     case.decode()
     torch.cuda.synchronize()
     return case
 
 
-def test_c4_sampled_rows_match_oracle(c4):
-    ids = c4.token_ids.cpu().numpy()
-    width = c4.width.cpu().numpy()
-    out = c4.out.cpu().numpy()
-    lse = c4.lse.cpu().numpy()
-    fetch = harness.device_kv_fetch(c4.k_cache, c4.v_cache)
+def test_full_decode_sampled_rows_match_oracle(full):
+    ids = full.token_ids.cpu().numpy()
+    width = full.width.cpu().numpy()
+    out = full.out.cpu().numpy()
+    lse = full.lse.cpu().numpy()
+    fetch = harness.device_kv_fetch(full.k_cache, full.v_cache)
     for r in SAMPLED_ROWS:
-        exp = harness.oracle_row(c4.data, r, kv_fetch=fetch)
+        exp = harness.oracle_row(full.data, r, kv_fetch=fetch)
         assert width[r] == 2048
         assert np.array_equal(ids[r, :2048], exp["ids"]), r
         err = harness.normwise_rel_err(out[r], exp["out_exact"])
@@ -41,30 +41,30 @@ def test_c4_sampled_rows_match_oracle(c4):
         assert np.allclose(lse[r], exp["lse_exact"], rtol=0, atol=1e-5)
 
 
-def test_c4_all_rows_structural(c4):
+def test_full_decode_all_rows_structural(full):
     """Every row: width 4k, strictly ascending group-aligned runs of four, no
     tail (262,144 = 4 x 65,536), -1 padding, finite outputs."""
-    ids = c4.token_ids.cpu().numpy()
-    assert np.all(c4.width.cpu().numpy() == 2048)
+    ids = full.token_ids.cpu().numpy()
+    assert np.all(full.width.cpu().numpy() == 2048)
     body = ids[:, :2048].reshape(32, 512, 4)
     assert np.all(body[:, :, 0] % 4 == 0)
     assert np.all(body - body[:, :, :1] == np.arange(4))
     assert np.all(np.diff(body[:, :, 0], axis=1) > 0)
     assert np.all(ids[:, 2048:] == -1)
-    assert torch.isfinite(c4.out).all() and torch.isfinite(c4.lse).all()
+    assert torch.isfinite(full.out).all() and torch.isfinite(full.lse).all()
 
 
-def test_c4_repeat_is_bitwise_identical(c4):
-    ref = (c4.token_ids.clone(), c4.out.clone(), c4.lse.clone())
-    c4.decode()
+def test_full_decode_repeat_is_bitwise_identical(full):
+    ref = (full.token_ids.clone(), full.out.clone(), full.lse.clone())
+    full.decode()
     torch.cuda.synchronize()
-    assert torch.equal(ref[0], c4.token_ids)
-    assert torch.equal(ref[1], c4.out) and torch.equal(ref[2], c4.lse)
+    assert torch.equal(ref[0], full.token_ids)
+    assert torch.equal(ref[1], full.out) and torch.equal(ref[2], full.lse)
 
 
-def test_c4_fused_equals_compact(c4):
-    ref = (c4.token_ids.clone(), c4.width.clone(), c4.out.clone(), c4.lse.clone())
-    c4.decode(fused=True)
+def test_full_decode_fused_equals_compact(full):
+    ref = (full.token_ids.clone(), full.width.clone(), full.out.clone(), full.lse.clone())
+    full.decode(fused=True)
     torch.cuda.synchronize()
-    assert torch.equal(ref[0], c4.token_ids) and torch.equal(ref[1], c4.width)
-    assert torch.equal(ref[2], c4.out) and torch.equal(ref[3], c4.lse)
+    assert torch.equal(ref[0], full.token_ids) and torch.equal(ref[1], full.width)
+    assert torch.equal(ref[2], full.out) and torch.equal(ref[3], full.lse)

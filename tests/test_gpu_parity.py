@@ -53,7 +53,7 @@ def check_rows(case, rows=None, tol=ATTN_TOL, kv_fetch=None):
         assert np.allclose(lse[r], exp["lse_exact"], rtol=0, atol=1e-5), (s.name, r)
 
 
-@pytest.fixture(scope="module", params=["c1", "c2", "c3"])
+@pytest.fixture(scope="module", params=["tail_2055", "ring_65537", "dup_100000"])
 def named(request):
     data = inputs.make(inputs.spec(request.param), seed=1, device="cpu")
     case = harness.GpuCase(data)

@@ -344,7 +344,7 @@ def test_attend_online_within_bound_of_exact(w, h_q, h_kv, d):
 
 # ------------------------------------------------------ full row invariants
 
-def _c1_row(n_tokens, data):
+def _tail_row(n_tokens, data):
     raw = data["raw_keys"].numpy()
     pooled = oracle.pool_full(raw[:n_tokens])
     scale = float(np.float32(1 / np.sqrt(64)))
@@ -358,8 +358,8 @@ def _c1_row(n_tokens, data):
 def test_dense_parity_sweep_attention(n):
     """At or below budget the sparse row equals the dense causal row, bit for
     bit, attention output included; just past the cut it does not."""
-    data = inputs.make(inputs.spec("c1"), seed=1)
-    sparse = _c1_row(n, data)
+    data = inputs.make(inputs.spec("tail_2055"), seed=1)
+    sparse = _tail_row(n, data)
     scale = float(np.float32(1 / np.sqrt(64)))
     dense = oracle.dense_row(n, data["slot_map"].numpy(), data["kv_slots"],
                              data["k_cache"].numpy(), data["v_cache"].numpy(),
@@ -376,9 +376,9 @@ def test_dense_parity_sweep_attention(n):
         assert dropped not in kept and len(kept) == 512
 
 
-def test_c1_full_row_invariants():
-    data = inputs.make(inputs.spec("c1"), seed=2)
-    r = _c1_row(2055, data)
+def test_tail_2055_full_row_invariants():
+    data = inputs.make(inputs.spec("tail_2055"), seed=2)
+    r = _tail_row(2055, data)
     assert r["width"] == 2051                          # 512 groups * 4 + 3 tail
     chosen = r["ids"][:2048:4] // 4
     check_row_shape(r["ids"], chosen, 2055)
@@ -408,9 +408,9 @@ def test_chunk_rows_equal_independent_decode_rows():
 
 
 def test_inputs_are_seeded_and_device_independent_in_shape():
-    a = inputs.make(inputs.spec("c1"), seed=5)
-    b = inputs.make(inputs.spec("c1"), seed=5)
+    a = inputs.make(inputs.spec("tail_2055"), seed=5)
+    b = inputs.make(inputs.spec("tail_2055"), seed=5)
     for key in ("index_q", "raw_keys", "q", "k_cache", "v_cache", "slot_map"):
         assert torch.equal(a[key], b[key])
-    c = inputs.make(inputs.spec("c1"), seed=6)
+    c = inputs.make(inputs.spec("tail_2055"), seed=6)
     assert not torch.equal(a["raw_keys"], c["raw_keys"])
