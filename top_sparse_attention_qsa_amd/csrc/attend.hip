@@ -127,7 +127,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact or cache rows
 
   // Every load is unconditional: rows past a chunk's width read the chunk's
-  // last valid row (always in bounds); their K rows are zeroed in LDS and
+  // last valid row (always in bounds); their scores are replaced by -inf and
   // their weights p are 0, so they add nothing.  No load sits behind a branch.
   // Prefetches are unconditional as well: an empty or out-of-range next item
   // loads (and ignores) row 0 of the last item's chunk, which always exists.
@@ -247,15 +247,17 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     // An item with no rows (cn == 0) runs the same code on masked rows and
     // skips its stores, so every prefetch is issued from one program point.
     {
-      // stage this item's K in LDS (rows past the width are zero; rows whose
-      // ID or slot was out of range are NaN, as in the compact path)
+      // stage this item's K in LDS (rows past the width hold a copy of the
+      // last row -- their scores are replaced by -inf, so they are never
+      // used; rows whose ID or slot was out of range are NaN, as in the
+      // compact path)
       __syncthreads();  // the previous item is done with LDS
 #pragma unroll
       for (int r = 0; r < KV4; ++r) {
         const int e = tid + r * NT;
         const int i = e / (D / 4);
         const int c = e - i * (D / 4);
-        float4 kv = i < cn ? kst[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 kv = kst[r];
         if constexpr (FUSED) {
           if (i < cn && ring[rs_cur][i] < 0) {
             const float nan = __int_as_float(0x7fc00000);
