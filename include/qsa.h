@@ -125,8 +125,8 @@ typedef struct qsa_bytes {
  *             slot_map[slot_off[b] + t].
  * k_cache,    [S][H_kv][D] f32.
  * v_cache
- * k_compact,  [rows][4k+4][H_kv][D] f32; rows at or past width untouched.
- * v_compact
+ * k_compact,  [rows][H_kv][4k+4][D] f32: each KV head's selected rows of a
+ * v_compact   query row are contiguous; positions at or past width untouched.
  * q           [rows][H_q][D] f32.  out [rows][H_q][D] f32; lse [rows][H_q].
  */
 

@@ -134,7 +134,8 @@ def test_select_then_emit_equals_fused(named):
 
 def test_gather_bitexact(named):
     s, sh = named.spec, named.shape
-    kc = torch.full((s.rows, sh.token_stride, s.h_kv, s.d), 7.0, device="cuda")
+    # compact layout [row][KV head][position][dim]
+    kc = torch.full((s.rows, s.h_kv, sh.token_stride, s.d), 7.0, device="cuda")
     vc = torch.full_like(kc, 7.0)
     phys = torch.full((s.rows, sh.token_stride), -7, dtype=torch.int32, device="cuda")
     qsa.qsa_resolve_gather(sh, named.token_ids, named.width, named.seq_len, named.slot_map,
@@ -145,14 +146,16 @@ def test_gather_bitexact(named):
         w = len(exp["ids"])
         assert np.array_equal(phys[r, :w], exp["slots"])
         assert np.all(phys[r, w:] == -7)
-        assert kc[r, :w].tobytes() == exp["kx"].tobytes()
-        assert vc[r, :w].tobytes() == exp["vx"].tobytes()
-        assert np.all(kc[r, w:] == 7.0)
+        kx = np.ascontiguousarray(kc[r, :, :w].transpose(1, 0, 2))
+        vx = np.ascontiguousarray(vc[r, :, :w].transpose(1, 0, 2))
+        assert kx.tobytes() == exp["kx"].tobytes()
+        assert vx.tobytes() == exp["vx"].tobytes()
+        assert np.all(kc[r, :, w:] == 7.0)
 
 
 def test_standalone_attend_equals_decode(named):
     s, sh = named.spec, named.shape
-    kc = torch.empty((s.rows, sh.token_stride, s.h_kv, s.d), device="cuda")
+    kc = torch.empty((s.rows, s.h_kv, sh.token_stride, s.d), device="cuda")
     vc = torch.empty_like(kc)
     qsa.qsa_resolve_gather(sh, named.token_ids, named.width, named.seq_len, named.slot_map,
                            named.slot_off, named.k_cache, named.v_cache, kc, vc)
@@ -293,12 +296,12 @@ def test_out_of_range_slots_give_nan_rows():
     case.decode()
     torch.cuda.synchronize()
     sh = case.shape
-    kc = torch.zeros((1, sh.token_stride, 1, 64), device="cuda")
+    kc = torch.zeros((1, 1, sh.token_stride, 64), device="cuda")
     vc = torch.zeros_like(kc)
     phys = torch.zeros((1, sh.token_stride), dtype=torch.int32, device="cuda")
     qsa.qsa_resolve_gather(sh, case.token_ids, case.width, case.seq_len, case.slot_map,
                            case.slot_off, case.k_cache, case.v_cache, kc, vc, phys)
-    assert int(phys[0, 5]) == -1 and torch.isnan(kc[0, 5]).all()
+    assert int(phys[0, 5]) == -1 and torch.isnan(kc[0, 0, 5]).all()
     assert torch.isnan(case.out[0]).all()
 
 

@@ -37,6 +37,7 @@ struct AttnCfg {
   static constexpr int KP = D + 4;       // padded K row, floats
   static constexpr int DPL = D / kWave;  // output dims per lane
   static constexpr int KV4 = C * D / 4 / NT;  // K float4 per thread per chunk
+  static constexpr int QV4 = (GQ * D / 4 + NT - 1) / NT;  // q float4 per thread per item
   static constexpr int KFLOATS = C * KP;
   static constexpr int RFLOATS = NW * GQ * D;  // per-wavefront P.V partials, aliasing K
   static constexpr int SFLOATS = KFLOATS > RFLOATS ? KFLOATS : RFLOATS;
@@ -104,8 +105,11 @@ struct RowSource {
   int32_t queries;
 };
 
+// Three resident workgroups per compute unit (at most 168 VGPRs) where the
+// GQA group fits them without spills.
 template <int D, int GQ, int MODE>
 __global__ void __launch_bounds__(4 * kWave)
+__attribute__((amdgpu_waves_per_eu(D * GQ <= 1024 ? 3 : 2)))
 attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* __restrict__ width,
                     int32_t q_heads, int32_t kv_heads, int32_t stride, int32_t n_chunks,
                     float scale, int64_t row0, int64_t rows, float* __restrict__ part_acc,
@@ -113,8 +117,9 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   using A = AttnCfg<D, GQ>;
   constexpr bool FUSED = MODE != kCompact;
   constexpr int NW = A::NW, NT = A::NT, HPW = A::HPW, KPW = A::KPW, KP = A::KP;
-  constexpr int DPL = A::DPL, KV4 = A::KV4;
+  constexpr int DPL = A::DPL, KV4 = A::KV4, QV4 = A::QV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
+  __shared__ float4 ql4[GQ * D / 4];          // the item's query heads
   __shared__ float4 ps4[GQ * C / 4];
   __shared__ int32_t ring[FUSED ? 3 : 1][C];  // resolved slots (-1: invalid ID or slot)
   float* smem = reinterpret_cast<float*>(smem4);
@@ -144,12 +149,16 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       const int32_t sl = ring[ring_slot][i];
       return cache + (int64_t)(sl >= 0 ? sl : 0) * rstride + (int64_t)x.hk * D;
     } else {
-      return compact + ((x.lrow * stride + (int64_t)x.chunk * C + i) * kv_heads + x.hk) *
+      return compact + ((x.lrow * kv_heads + x.hk) * stride + (int64_t)x.chunk * C + i) *
                            (int64_t)D;
     }
   };
   float4 kst[KV4];
+  float4 qst[QV4];
   float vreg[KPW][DPL];
+  // K rows and the query heads of item x (q staged in LDS next to K, so the
+  // score loop reads it with broadcast LDS loads instead of scalar loads
+  // that would each wait on a cache round trip)
   auto load_k = [&](const Item& x, int cn_raw, int ring_slot) {
     const int cn = cn_raw > 0 ? cn_raw : 1;
 #pragma unroll
@@ -160,6 +169,12 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       const int ic = i < cn ? i : cn - 1;
       kst[r] = *reinterpret_cast<const float4*>(
           row_ptr(src.k_compact, src.k_cache, x, ic, ring_slot) + 4 * c);
+    }
+    const float* qg = q + ((row0 + x.lrow) * q_heads + (int64_t)x.hk * GQ) * D;
+#pragma unroll
+    for (int r = 0; r < QV4; ++r) {
+      const int e = tid + r * NT;
+      qst[r] = *reinterpret_cast<const float4*>(qg + 4 * (e < GQ * D / 4 ? e : 0));
     }
   };
   auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
@@ -266,6 +281,11 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         }
         smem4[(i * KP) / 4 + c] = kv;
       }
+#pragma unroll
+      for (int r = 0; r < QV4; ++r) {
+        const int e = tid + r * NT;
+        if (e < GQ * D / 4) ql4[e] = qst[r];
+      }
       __syncthreads();
       // next item's K streams in under this item; the scheduling barriers keep
       // the compiler from hoisting it (or V below) above the last use of the
@@ -275,28 +295,25 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       resolve_ids(nxt2, cn_next2);
 
       // scores for this wavefront's query heads: lane = compact row
-      const int64_t row = row0 + cur.lrow;
-      // with GQ < 4 the wavefronts past the last head only clamp their head
-      // index (in bounds) and discard the result
-      const float* qrow[HPW];
+      // (with GQ < 4 the wavefronts past the last head only clamp their head
+      // index and discard the result)
+      int hl[HPW];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const int hl = wave * HPW + hh < GQ ? wave * HPW + hh : GQ - 1;
-        qrow[hh] = q + (row * q_heads + (int64_t)cur.hk * GQ + hl) * D;
-      }
+      for (int hh = 0; hh < HPW; ++hh) hl[hh] = wave * HPW + hh < GQ ? wave * HPW + hh : GQ - 1;
       float dot[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) dot[hh] = 0.0f;
-#pragma unroll 4
+#pragma unroll 2
       for (int d = 0; d < D; d += 4) {
         const float4 k4 = *reinterpret_cast<const float4*>(smem + lane * KP + d);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
+          const float4 q4 = ql4[(hl[hh] * D + d) / 4];
           float a = dot[hh];
-          a = __builtin_fmaf(qrow[hh][d + 0], k4.x, a);
-          a = __builtin_fmaf(qrow[hh][d + 1], k4.y, a);
-          a = __builtin_fmaf(qrow[hh][d + 2], k4.z, a);
-          a = __builtin_fmaf(qrow[hh][d + 3], k4.w, a);
+          a = __builtin_fmaf(q4.x, k4.x, a);
+          a = __builtin_fmaf(q4.y, k4.y, a);
+          a = __builtin_fmaf(q4.z, k4.z, a);
+          a = __builtin_fmaf(q4.w, k4.w, a);
           dot[hh] = a;
         }
       }

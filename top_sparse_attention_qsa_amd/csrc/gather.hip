@@ -8,9 +8,11 @@
 //
 // A workgroup handles kGatherTokens compact rows of one query row: the first
 // lanes resolve the slots into LDS, then all 256 threads stream the H_kv*D
-// floats of each K and V row with float4 loads and stores (2 KiB contiguous
-// per row at H_kv=4, D=128).  Out-of-range IDs or slots produce NaN rows and
-// slot -1 instead of a fault.
+// floats of each K and V cache row with float4 loads (2 KiB contiguous per
+// row at H_kv=4, D=128) and store each KV head's D floats into that head's
+// run of the compact scratch ([row][KV head][position][dim]), which the
+// attention then reads as one contiguous block per (row, head, chunk).
+// Out-of-range IDs or slots produce NaN rows and slot -1 instead of a fault.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -20,7 +22,7 @@ __global__ void __launch_bounds__(256)
 gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__ width,
               const int32_t* __restrict__ seq_len, const int32_t* __restrict__ slot_map,
               const int64_t* __restrict__ slot_off, const float4* __restrict__ k_cache,
-              const float4* __restrict__ v_cache, int32_t queries, int32_t row_f4,
+              const float4* __restrict__ v_cache, int32_t queries, int32_t row_f4, int32_t head_f4,
               int32_t stride, int64_t kv_slots, int64_t row0, float4* __restrict__ k_out,
               float4* __restrict__ v_out, int32_t* __restrict__ phys_slots) {
   __shared__ int32_t slot_sh[kGatherTokens];
@@ -77,7 +79,11 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
         const int c = e - t * row_f4;
         const int32_t slot = slot_sh[t];
         if (slot != -2) {
-          const int64_t dst = (lrow * stride + i0 + t) * (int64_t)row_f4 + c;
+          // compact layout [row][KV head][position][dim]: a head's rows of one
+          // query row are contiguous, so the attention streams them
+          const int hk = c / head_f4;
+          const int64_t dst = ((lrow * (row_f4 / head_f4) + hk) * stride + i0 + t) * head_f4 +
+                              (c - hk * head_f4);
           k_out[dst] = slot >= 0 ? kv[r] : make_float4(nan, nan, nan, nan);
           v_out[dst] = slot >= 0 ? vv[r] : make_float4(nan, nan, nan, nan);
         }
@@ -94,7 +100,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.stride + kGatherTokens - 1) / kGatherTokens), (unsigned)a.rows);
   hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, a.token_ids, a.width, a.seq_len,
                      a.slot_map, a.slot_off, reinterpret_cast<const float4*>(a.k_cache),
-                     reinterpret_cast<const float4*>(a.v_cache), a.queries, row_f4, a.stride,
+                     reinterpret_cast<const float4*>(a.v_cache), a.queries, row_f4,
+                     a.head_dim / 4, a.stride,
                      a.kv_slots, a.row0, reinterpret_cast<float4*>(a.k_compact),
                      reinterpret_cast<float4*>(a.v_compact), a.phys_slots);
   return hipGetLastError();
