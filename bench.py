@@ -121,10 +121,17 @@ def cpu_baseline(data, rows, threads):
         list(ex.map(phase2, prep))
         t3 = time.perf_counter()
     timed = (t1 - t0) + (t3 - t2)
+    # one row, one thread, for reference
+    p = prep[0]
+    t4 = time.perf_counter()
+    phase1(p)
+    phase2(p)
+    one_row = time.perf_counter() - t4
     return dict(value=len(rows) / timed, unit="queries/s", cores=threads, kind="oracle",
                 sample=f"all {len(rows)} rows of one decode step of the same workload "
                        f"(score+select+emit+resolve, then F32 online attention over the "
                        f"oracle's own gathered rows; pooling and the K/V row copy untimed)",
+                single_thread_row_s=one_row, cpu_model=cpu_model(),
                 seconds=timed)
 
 
@@ -177,6 +184,17 @@ def chunk_leg(seed, steps):
             "rows": rows, "steps": steps, **res}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_calibration(gib=1.0, reps=5):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -207,6 +225,7 @@ def main():
               f"multi-GPU leg (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import top_sparse_attention_qsa_amd as qsa
     from tests import harness, inputs
@@ -251,19 +270,23 @@ def main():
     def stage_loop(fused):
         """Per-kernel times: K more steps with a HIP event recorded on the
         launch stream at every stage boundary (these steps run slower than
-        the timed ones; each stage interval is one kernel)."""
+        the timed ones; each stage interval is one kernel).  Returns the mean
+        per stage and the p10/p50/p90 of the per-step and score-kernel times."""
         timer = qsa.Timer(args.steps)
         for _ in range(args.steps):
             case.decode(timer, fused=fused)
         torch.cuda.synchronize()
         stage = timer.read()
         timer.close()
-        return {name: sum(c[i] for c in stage) / len(stage)
-                for i, name in enumerate(qsa.STAGE_NAMES)}
+        means = {name: sum(c[i] for c in stage) / len(stage)
+                 for i, name in enumerate(qsa.STAGE_NAMES)}
+        pct = lambda v: {f"p{q}": float(np.percentile(v, q)) for q in (10, 50, 90)}
+        spread = {"step_ms": pct([sum(c) for c in stage]), "score_ms": pct([c[0] for c in stage])}
+        return means, spread
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     ms_per_step = timed_loop(False)
-    stage_ms = stage_loop(False)
+    stage_ms, stage_spread = stage_loop(False)
     score_ms = stage_ms["score"]
 
     # the same step with the gather fused into the attention (no compact scratch)
@@ -272,7 +295,7 @@ def main():
     for _ in range(args.warmup):
         case.decode(fused=True)
     fused_ms = timed_loop(True)
-    fused_stage_ms = stage_loop(True)
+    fused_stage_ms, _ = stage_loop(True)
     assert torch.equal(case.out, ref_out), "fused path differs from the compact path"
 
     alg = algorithmic_bytes()
@@ -309,6 +332,7 @@ def main():
         "stage_ms": stage_ms,
         "stage_ms_note": "HIP events at every stage boundary, in a loop of its own after the "
                          "timed steps",
+        "stage_spread": stage_spread,
         "roofline": {
             "kernel": "score_kernel<16,128>",
             "bound": "hbm",
