@@ -13,9 +13,10 @@
 //
 // attend_chunk_kernel: one workgroup per (chunk, KV head, row) serves every
 // query head of the KV head's GQA group (query head hq reads KV head
-// hq / (H_q/H_kv)).  Scores: the chunk's K rows are staged in LDS (rows padded
-// by 16 bytes so lane-per-row float4 reads are bank-conflict free), lane =
-// compact row, query from scalar loads.  P.V: wavefront w accumulates rows
+// hq / (H_q/H_kv)).  Scores: the chunk's K rows and query heads are staged
+// in LDS; wavefront w scores rows 16w..16w+15, lane (r, g) = row r with head
+// group g, so reads broadcast; the per-head chunk maximum is exchanged once
+// between the wavefronts.  P.V: wavefront w accumulates rows
 // [w*C/NW, (w+1)*C/NW) in row order with lane = output dimension, reading its
 // V rows straight from memory (issued before the score phase); the NW
 // partial sums are then added in wavefront order.  The chunk's accumulation
@@ -32,7 +33,7 @@ template <int D, int GQ>
 struct AttnCfg {
   static constexpr int NW = 4;           // wavefronts; with GQ < 4 some have no score work
   static constexpr int NT = NW * kWave;
-  static constexpr int HPW = (GQ + NW - 1) / NW;  // query heads per wavefront (score phase)
+  static constexpr int HPL = GQ >= NW ? GQ / NW : 1;  // query heads per lane (score phase)
   static constexpr int KPW = C / NW;     // compact rows per wavefront in the P.V phase
   static constexpr int KP = D + 4;       // padded K row, floats
   static constexpr int DPL = D / kWave;  // output dims per lane
@@ -116,12 +117,14 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
                     float* __restrict__ part_ml) {
   using A = AttnCfg<D, GQ>;
   constexpr bool FUSED = MODE != kCompact;
-  constexpr int NW = A::NW, NT = A::NT, HPW = A::HPW, KPW = A::KPW, KP = A::KP;
+  constexpr int NW = A::NW, NT = A::NT, HPL = A::HPL, KPW = A::KPW, KP = A::KP;
   constexpr int DPL = A::DPL, KV4 = A::KV4, QV4 = A::QV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
   __shared__ float4 ql4[GQ * D / 4];          // the item's query heads
   __shared__ float4 ps4[GQ * C / 4];
   __shared__ int32_t ring[FUSED ? 3 : 1][C];  // resolved slots (-1: invalid ID or slot)
+  __shared__ float mw_sh[NW][GQ];             // per wavefront and head: max over its 16 rows
+  __shared__ float lw_sh[NW][GQ];             // per wavefront and head: sum of its weights
   float* smem = reinterpret_cast<float*>(smem4);
   float* ps = reinterpret_cast<float*>(ps4);
 
@@ -294,20 +297,24 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       load_k(nxt, cn_next, rs_next);
       resolve_ids(nxt2, cn_next2);
 
-      // scores for this wavefront's query heads: lane = compact row
-      // (with GQ < 4 the wavefronts past the last head only clamp their head
-      // index and discard the result)
-      int hl[HPW];
+      // scores: lane (r16, g4) scores row 16*wave + r16 for query heads
+      // g4*HPL .. g4*HPL+HPL-1 (with GQ < 4, lanes of head groups past the
+      // last head clamp their head and discard the result).  Four lanes share
+      // each K row and sixteen each q row, so the LDS reads broadcast and a
+      // wavefront moves a quarter of the K bytes a lane-per-row mapping would.
+      const int r16 = lane & 15, g4 = lane >> 4;
+      const int ri = 16 * wave + r16;  // this lane's row of the chunk
+      int hl[HPL];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) hl[hh] = wave * HPW + hh < GQ ? wave * HPW + hh : GQ - 1;
-      float dot[HPW];
+      for (int hh = 0; hh < HPL; ++hh) hl[hh] = g4 * HPL + hh < GQ ? g4 * HPL + hh : GQ - 1;
+      float dot[HPL];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) dot[hh] = 0.0f;
+      for (int hh = 0; hh < HPL; ++hh) dot[hh] = 0.0f;
 #pragma unroll 2
       for (int d = 0; d < D; d += 4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(smem + lane * KP + d);
+        const float4 k4 = *reinterpret_cast<const float4*>(smem + ri * KP + d);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
+        for (int hh = 0; hh < HPL; ++hh) {
           const float4 q4 = ql4[(hl[hh] * D + d) / 4];
           float a = dot[hh];
           a = __builtin_fmaf(q4.x, k4.x, a);
@@ -317,21 +324,31 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
           dot[hh] = a;
         }
       }
-      const int64_t slot0 = (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_chunks + cur.chunk;
+      // softmax: the chunk maximum per head from the four wavefronts' row
+      // maxima, then this wavefront's weights and their sum
+      const bool rvalid = ri < cn;
+      float sc[HPL];
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const float sc = (lane < cn) ? dot[hh] * scale : -INFINITY;
-        const float m = wave_max(sc);
-        const float p = (lane < cn) ? expf(sc - m) : 0.0f;
-        const float l = wave_sum(p);
-        if (wave * HPW + hh >= GQ) continue;  // uniform: no such head
-        ps[(wave * HPW + hh) * C + lane] = p;
-        if (lane == 0 && cn > 0)
-          *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)(wave * HPW + hh) * n_chunks) * 2) =
-              make_float2(m, l);
+      for (int hh = 0; hh < HPL; ++hh) {
+        sc[hh] = rvalid ? dot[hh] * scale : -INFINITY;
+        const float mx = row_max16(sc[hh]);
+        if (r16 == 0 && g4 * HPL + hh < GQ) mw_sh[wave][g4 * HPL + hh] = mx;
       }
       resolve_slots(nxt2, cn_next2);
-      __syncthreads();  // ps complete; K no longer read, so smem can hold partials
+      __syncthreads();  // maxima exchanged; K no longer read, so smem can hold partials
+#pragma unroll
+      for (int hh = 0; hh < HPL; ++hh) {
+        const int h = hl[hh];
+        float m = mw_sh[0][h];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, mw_sh[w][h]);
+        const float p = rvalid ? expf(sc[hh] - m) : 0.0f;
+        const float l = row_sum16(p);
+        if (g4 * HPL + hh < GQ) {
+          ps[h * C + ri] = p;  // read back below by this wavefront only
+          if (r16 == 0) lw_sh[wave][h] = l;
+        }
+      }
 
       // P.V over this wavefront's rows, in row order; lane owns dims lane*DPL..
       float acc[GQ][DPL];
@@ -361,27 +378,27 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       load_v(nxt, cn_next, rs_next);  // next item's V streams in under the rest
 
       // combine the wavefronts' partial sums in wavefront order
-      if constexpr (NW == 1) {
-        if (cn > 0)
 #pragma unroll
-          for (int h = 0; h < GQ; ++h)
+      for (int h = 0; h < GQ; ++h)
 #pragma unroll
-            for (int t = 0; t < DPL; ++t)
-              part_acc[(slot0 + (int64_t)h * n_chunks) * D + lane * DPL + t] = acc[h][t];
-      } else {
+        for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
+      __syncthreads();
+      const int64_t slot0 = (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_chunks + cur.chunk;
+      if (tid < GQ && cn > 0) {
+        float m = mw_sh[0][tid];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h)
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, mw_sh[w][tid]);
+        const float l = (lw_sh[0][tid] + lw_sh[1][tid]) + (lw_sh[2][tid] + lw_sh[3][tid]);
+        *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)tid * n_chunks) * 2) =
+            make_float2(m, l);
+      }
+      for (int o = tid; o < (cn > 0 ? GQ * D : 0); o += NT) {
+        const int h = o / D;
+        const int d = o - h * D;
+        float sum = smem[h * D + d];
 #pragma unroll
-          for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
-        __syncthreads();
-        for (int o = tid; o < (cn > 0 ? GQ * D : 0); o += NT) {
-          const int h = o / D;
-          const int d = o - h * D;
-          float sum = smem[h * D + d];
-#pragma unroll
-          for (int ww = 1; ww < NW; ++ww) sum = sum + smem[(ww * GQ + h) * D + d];
-          part_acc[(slot0 + (int64_t)h * n_chunks) * D + d] = sum;
-        }
+        for (int ww = 1; ww < NW; ++ww) sum = sum + smem[(ww * GQ + h) * D + d];
+        part_acc[(slot0 + (int64_t)h * n_chunks) * D + d] = sum;
       }
       resolve_store(FUSED ? (j + 2) % 3 : 0);  // visible after the next item's first barrier
     }

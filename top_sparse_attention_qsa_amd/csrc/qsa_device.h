@@ -93,6 +93,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
+// Maximum over the 16 lanes of this lane's DPP row (every lane of the row
+// receives it; exact, so all agree).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<kRowRor1>(v));
+  v = fmaxf(v, dpp_f32<kRowRor2>(v));
+  v = fmaxf(v, dpp_f32<kRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kRowRor8>(v));
+  return v;
+}
+
+// Sum over the 16 lanes of this lane's DPP row.  Lanes associate the terms in
+// different orders, so only one fixed lane's value is used.
+__device__ __forceinline__ float row_sum16(float v) {
+  v = v + dpp_f32<kRowRor1>(v);
+  v = v + dpp_f32<kRowRor2>(v);
+  v = v + dpp_f32<kRowRor4>(v);
+  v = v + dpp_f32<kRowRor8>(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v = v + dpp_f32<kRowRor1>(v);
   v = v + dpp_f32<kRowRor2>(v);
