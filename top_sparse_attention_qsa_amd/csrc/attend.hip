@@ -14,9 +14,9 @@
 // attend_chunk_kernel: one workgroup per (chunk, KV head, row) serves every
 // query head of the KV head's GQA group (query head hq reads KV head
 // hq / (H_q/H_kv)).  Scores: the chunk's K rows and query heads are staged
-// in LDS; wavefront w scores rows 16w..16w+15, lane (r, g) = row r with head
-// group g, so reads broadcast; the per-head chunk maximum is exchanged once
-// between the wavefronts.  P.V: wavefront w accumulates rows
+// in LDS; wavefront w scores rows 16w..16w+15 for every head of the group on
+// v_mfma_f32_16x16x4_f32 (one column per head); the per-head chunk maximum is
+// exchanged once between the wavefronts.  P.V: wavefront w accumulates rows
 // [w*C/NW, (w+1)*C/NW) in row order with lane = output dimension, reading its
 // V rows straight from memory (issued before the score phase); the NW
 // partial sums are then added in wavefront order.  The chunk's accumulation
@@ -29,11 +29,17 @@ namespace {
 
 constexpr int C = kAttnChunk;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D, int GQ>
 struct AttnCfg {
   static constexpr int NW = 4;           // wavefronts; with GQ < 4 some have no score work
   static constexpr int NT = NW * kWave;
-  static constexpr int HPL = GQ >= NW ? GQ / NW : 1;  // query heads per lane (score phase)
+  static_assert(GQ <= 16, "one MFMA column per query head");
   static constexpr int KPW = C / NW;     // compact rows per wavefront in the P.V phase
   static constexpr int KP = D + 4;       // padded K row, floats
   static constexpr int DPL = D / kWave;  // output dims per lane
@@ -117,7 +123,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
                     float* __restrict__ part_ml) {
   using A = AttnCfg<D, GQ>;
   constexpr bool FUSED = MODE != kCompact;
-  constexpr int NW = A::NW, NT = A::NT, HPL = A::HPL, KPW = A::KPW, KP = A::KP;
+  constexpr int NW = A::NW, NT = A::NT, KPW = A::KPW, KP = A::KP;
   constexpr int DPL = A::DPL, KV4 = A::KV4, QV4 = A::QV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
   __shared__ float4 ql4[GQ * D / 4];          // the item's query heads
@@ -297,56 +303,55 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       load_k(nxt, cn_next, rs_next);
       resolve_ids(nxt2, cn_next2);
 
-      // scores: lane (r16, g4) scores row 16*wave + r16 for query heads
-      // g4*HPL .. g4*HPL+HPL-1 (with GQ < 4, lanes of head groups past the
-      // last head clamp their head and discard the result).  Four lanes share
-      // each K row and sixteen each q row, so the LDS reads broadcast and a
-      // wavefront moves a quarter of the K bytes a lane-per-row mapping would.
-      const int r16 = lane & 15, g4 = lane >> 4;
-      const int ri = 16 * wave + r16;  // this lane's row of the chunk
-      int hl[HPL];
+      // scores on v_mfma_f32_16x16x4_f32: S[row 16w + 4lq + r][head li] in
+      // sacc[r] (lane (li, lq) = lane % 16, lane / 16); k-step (c, e) covers
+      // dim 16c + 4lq + e in both operands; head columns past the group read
+      // zeros.  Four independent accumulators, one per e, added at the end.
+      const int li = lane & 15, lq = lane >> 4;
+      const bool hcol = li < GQ;
+      f32x4 sp[4];
 #pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) hl[hh] = g4 * HPL + hh < GQ ? g4 * HPL + hh : GQ - 1;
-      float dot[HPL];
+      for (int e = 0; e < 4; ++e) sp[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) dot[hh] = 0.0f;
-#pragma unroll 2
-      for (int d = 0; d < D; d += 4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(smem + ri * KP + d);
-#pragma unroll
-        for (int hh = 0; hh < HPL; ++hh) {
-          const float4 q4 = ql4[(hl[hh] * D + d) / 4];
-          float a = dot[hh];
-          a = __builtin_fmaf(q4.x, k4.x, a);
-          a = __builtin_fmaf(q4.y, k4.y, a);
-          a = __builtin_fmaf(q4.z, k4.z, a);
-          a = __builtin_fmaf(q4.w, k4.w, a);
-          dot[hh] = a;
-        }
+      for (int c = 0; c < D / 16; ++c) {
+        const float4 a4 = smem4[((16 * wave + li) * KP + 16 * c + 4 * lq) / 4];
+        float4 b4 = ql4[((hcol ? li : 0) * D + 16 * c + 4 * lq) / 4];
+        if (!hcol) b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        sp[0] = mfma4(a4.x, b4.x, sp[0]);
+        sp[1] = mfma4(a4.y, b4.y, sp[1]);
+        sp[2] = mfma4(a4.z, b4.z, sp[2]);
+        sp[3] = mfma4(a4.w, b4.w, sp[3]);
       }
-      // softmax: the chunk maximum per head from the four wavefronts' row
-      // maxima, then this wavefront's weights and their sum
-      const bool rvalid = ri < cn;
-      float sc[HPL];
+      const f32x4 sacc = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+      // softmax: the chunk maximum per head from the four wavefronts' maxima
+      // over their 16 rows, then this wavefront's weights and their sum
+      const int rbase = 16 * wave + 4 * lq;  // rows rbase .. rbase+3 in this lane
+      float sc[4];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) {
-        sc[hh] = rvalid ? dot[hh] * scale : -INFINITY;
-        const float mx = row_max16(sc[hh]);
-        if (r16 == 0 && g4 * HPL + hh < GQ) mw_sh[wave][g4 * HPL + hh] = mx;
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = rbase + r < cn ? sacc[r] * scale : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
       }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if (lq == 0 && hcol) mw_sh[wave][li] = mx;
       resolve_slots(nxt2, cn_next2);
       __syncthreads();  // maxima exchanged; K no longer read, so smem can hold partials
-#pragma unroll
-      for (int hh = 0; hh < HPL; ++hh) {
-        const int h = hl[hh];
+      {
+        const int h = hcol ? li : 0;
         float m = mw_sh[0][h];
 #pragma unroll
         for (int w = 1; w < NW; ++w) m = fmaxf(m, mw_sh[w][h]);
-        const float p = rvalid ? expf(sc[hh] - m) : 0.0f;
-        const float l = row_sum16(p);
-        if (g4 * HPL + hh < GQ) {
-          ps[h * C + ri] = p;  // read back below by this wavefront only
-          if (r16 == 0) lw_sh[wave][h] = l;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = rbase + r < cn ? expf(sc[r] - m) : 0.0f;
+        float l = ((p[0] + p[1]) + p[2]) + p[3];
+        l = l + __shfl_xor(l, 16, kWave);
+        l = l + __shfl_xor(l, 32, kWave);
+        if (hcol) {
+          ps4[(h * C + rbase) / 4] = make_float4(p[0], p[1], p[2], p[3]);  // read back below
+          if (lq == 0) lw_sh[wave][h] = l;                                   // by this wavefront
         }
       }
 
