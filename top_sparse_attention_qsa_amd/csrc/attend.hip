@@ -306,12 +306,13 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       // scores on v_mfma_f32_16x16x4_f32: S[row 16w + 4lq + r][head li] in
       // sacc[r] (lane (li, lq) = lane % 16, lane / 16); k-step (c, e) covers
       // dim 16c + 4lq + e in both operands; head columns past the group read
-      // zeros.  Four independent accumulators, one per e, added at the end.
+      // zeros.  Two independent accumulators (even and odd e), added at the
+      // end.
       const int li = lane & 15, lq = lane >> 4;
       const bool hcol = li < GQ;
-      f32x4 sp[4];
+      f32x4 sp[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sp[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int e = 0; e < 2; ++e) sp[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const float4 a4 = smem4[((16 * wave + li) * KP + 16 * c + 4 * lq) / 4];
@@ -319,10 +320,10 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         if (!hcol) b4 = make_float4(0.f, 0.f, 0.f, 0.f);
         sp[0] = mfma4(a4.x, b4.x, sp[0]);
         sp[1] = mfma4(a4.y, b4.y, sp[1]);
-        sp[2] = mfma4(a4.z, b4.z, sp[2]);
-        sp[3] = mfma4(a4.w, b4.w, sp[3]);
+        sp[0] = mfma4(a4.z, b4.z, sp[0]);
+        sp[1] = mfma4(a4.w, b4.w, sp[1]);
       }
-      const f32x4 sacc = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+      const f32x4 sacc = sp[0] + sp[1];
       // softmax: the chunk maximum per head from the four wavefronts' maxima
       // over their 16 rows, then this wavefront's weights and their sum
       const int rbase = 16 * wave + 4 * lq;  // rows rbase .. rbase+3 in this lane
