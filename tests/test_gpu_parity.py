@@ -247,6 +247,19 @@ def test_all_scores_tied_streaming_path():
     assert np.array_equal(ids[0, :2048], np.arange(2048))
 
 
+def test_rows_longer_than_the_staged_maxima():
+    """More than 4,096 segment maxima (G > 65,536 groups): the selection
+    folds the maxima up to 8:1 and scans the whole row; a zero query on a
+    long row streams every key (all tied)."""
+    spec = inputs.custom("long", [600001, 300000], h_i=4, d_i=32, h_q=2, h_kv=1, d=64,
+                         keys="normal", slots="perm")
+    run_and_check(spec, seed=31)
+    spec = inputs.custom("long_ties", [400003], h_i=4, d_i=32, h_q=1, h_kv=1, d=64,
+                         keys="zero_query")
+    case = run_and_check(spec, seed=32)
+    assert np.array_equal(case.token_ids[0, :2048].cpu().numpy(), np.arange(2048))
+
+
 def test_tie_heavy_grid_duplicates():
     spec = inputs.custom("dups", [30000, 12345], h_i=8, d_i=64, h_q=8, h_kv=1, d=128,
                          keys="grid_dup", slots="perm")
