@@ -18,6 +18,14 @@
 namespace qsa {
 namespace {
 
+// Cache rows are read once per step: nontemporal loads keep them from
+// displacing the compact rows, which the attention reads next.
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __global__ void __launch_bounds__(256)
 gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__ width,
               const int32_t* __restrict__ seq_len, const int32_t* __restrict__ slot_map,
@@ -68,8 +76,8 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
       const int c = e - t * row_f4;
       const int32_t slot = slot_sh[t];
       const int64_t src = (int64_t)(slot >= 0 ? slot : 0) * row_f4 + c;
-      kv[r] = k_cache[src];
-      vv[r] = v_cache[src];
+      kv[r] = load_stream(k_cache + src);
+      vv[r] = load_stream(v_cache + src);
     }
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
