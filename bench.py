@@ -66,17 +66,86 @@ def source_digest():
     return h.hexdigest()
 
 
+def library_digest():
+    """Digest of every HIP source of the library (the step's kernels)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "top_sparse_attention_qsa_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counters():
+    try:
+        with open(COUNTERS) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
 def measured_traffic():
     """HBM bytes per score launch from the committed rocprofv3 counter
     summary, or None when absent or taken on a different kernel source."""
-    try:
-        with open(COUNTERS) as f:
-            c = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if c.get("source_sha256") != source_digest():
+    c = _counters()
+    if c is None or c.get("source_sha256") != source_digest():
         return None
     return c.get("traffic_bytes_per_launch")
+
+
+def measured_step_traffic():
+    """HBM bytes per decode step by stage (FETCH_SIZE + WRITE_SIZE of each
+    kernel, scaled by the copy calibration), or None when the counters were
+    taken on a different library source."""
+    c = _counters()
+    if c is None or c.get("library_sha256") != library_digest():
+        return None
+    return c.get("stage_traffic_bytes")
+
+
+def context_bandwidth(reps=10):
+    """Achievable-bandwidth context, not a denominator of anything reported:
+    a plain streaming read of 1 GiB (bwprobe/stream_read.hip, grid-stride
+    float4 loads) and torch's device copy of 1 GiB."""
+    import ctypes
+    import torch
+    from top_sparse_attention_qsa_amd import build as qsa_build
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    res = {}
+    fns = [("copy", lambda: y.copy_(x), 8 * n)]
+    if os.path.exists(qsa_build.BW_LIB):
+        bw = ctypes.CDLL(qsa_build.BW_LIB)
+        bw.bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+
+        def read():
+            s = torch.cuda.current_stream().cuda_stream
+            if bw.bw_stream_read(x.data_ptr(), 4 * n, sink.data_ptr(), s) != 0:
+                raise RuntimeError("bw_stream_read failed")
+        fns.insert(0, ("stream_read", read, 4 * n))
+    for name, fn, nbytes in fns:
+        for _ in range(3):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"{name}_gbps"] = nbytes / (ms * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    res["note"] = ("1 GiB of f32: a grid-stride streaming read kernel, and torch's device copy "
+                   "(bytes read + written); context only")
+    return res
 
 
 def cpu_baseline(data, rows, threads, passes=2):
@@ -306,6 +375,18 @@ def main():
     step_bytes = sum(alg.values())
     achieved = alg["score"] / (score_ms * 1e-3) / 1e9
     traffic = measured_traffic()
+    stage_traffic = measured_step_traffic()
+    step_traffic = None
+    if stage_traffic:
+        tb = sum(stage_traffic.values())
+        step_traffic = {
+            "bytes": tb, "over_algorithmic": tb / step_bytes,
+            "gbps_over_kernel_time": tb / (sum(stage_ms.values()) * 1e-3) / 1e9,
+            "by_stage": stage_traffic,
+            "source": "rocprofv3 FETCH_SIZE and WRITE_SIZE per kernel, scaled by a 1 GiB copy "
+                      "(profiles/decode_32x262144_counters.md)"}
+    print("[bench] context bandwidth", file=sys.stderr, flush=True)
+    context = context_bandwidth()
     widths = case.width.cpu()
     assert int(widths.min()) == 2048 and int(widths.max()) == 2048, "unexpected widths"
 
@@ -337,6 +418,8 @@ def main():
         "stage_ms_note": "HIP events at every stage boundary, in a loop of its own after the "
                          "timed steps",
         "stage_spread": stage_spread,
+        "step_traffic": step_traffic,
+        "context_bandwidth": context,
         "roofline": {
             "kernel": "score_kernel<16,128>",
             "bound": "hbm",

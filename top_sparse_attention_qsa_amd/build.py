@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
+# a streaming-read kernel for the benchmark's bandwidth context line (not libqsa)
+BW_SRC = os.path.join(PKG, "bwprobe", "stream_read.hip")
+BW_LIB = os.path.join(PKG, "bwprobe", "libbwprobe.so")
 BUILD = os.path.join(ROOT, "_build", "qsa")
 
 ARCH = "gfx950"
@@ -59,8 +62,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = BW_LIB + ".tmp"
+    cmd = [hipcc(), *HIPFLAGS, "-shared", "-o", tmp, BW_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {BW_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BW_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BW_LIB}")
     return LIB
 
 
