@@ -33,10 +33,9 @@ constexpr int NWAVES = NT / kWave;
 constexpr int kMaxStage = 4096;   // segment maxima staged in LDS (G <= 65,536)
 constexpr int kPerThread = 32;    // scores held per thread in one streaming pass
 
-struct SelectShared {
-  uint32_t hist[256];
+struct alignas(16) SelectShared {
+  uint32_t hist[3][256];  // radix passes rotate through three histograms
   uint32_t wave_tot[NWAVES];
-  uint32_t scal[4];
   uint32_t cand_key[kCandCap];
   uint32_t cand_pos[kCandCap];
   uint32_t maxima[kMaxStage];
@@ -66,14 +65,27 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 // With fewer than four passes the result is the k-th largest key with its
 // undecided low bits cleared -- a lower bound of it -- and the count is that
 // of keys above the decided prefix.
+//
+// One barrier per pass: every wavefront finds the digit from the pass's
+// histogram itself (the same values, so the same digit), and the passes
+// rotate through three histograms, so the one a pass clears for its
+// successor was last read two passes earlier, before the previous pass's
+// barrier.  On entry no wavefront may still read sh.hist (the caller has
+// passed a barrier since the last call).
 template <class Src, int PASSES = 4>
 __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, SelectShared& sh,
                                   uint32_t* t_out, uint32_t* above_out) {
   const int tid = (int)threadIdx.x;
+  const int lane = lane_id();
   uint32_t prefix = 0, mask = 0, kk = k, above = 0;
-  for (int shift = 24; shift >= 32 - 8 * PASSES; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
+  for (int i = tid; i < 256; i += NT) sh.hist[0][i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int shift = 24 - 8 * p;
+    uint32_t* hist = sh.hist[p % 3];
+    if (p + 1 < PASSES)
+      for (int i = tid; i < 256; i += NT) sh.hist[(p + 1) % 3][i] = 0;
     const uint32_t n_up = (n + NT - 1) / NT * NT;   // whole wavefronts stay converged
     for (uint32_t i = tid; i < n_up; i += NT) {
       bool act = false;
@@ -83,39 +95,37 @@ __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, Select
         act = (key & mask) == prefix;
         bin = (key >> shift) & 255u;
       }
-      hist_add(sh.hist, bin, act);
+      hist_add(hist, bin, act);
     }
     __syncthreads();
-    if (tid < kWave) {
-      // lane l owns bins 4l..4l+3; find the bin holding the kk-th largest
-      const int l = tid;
-      const uint32_t h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1];
-      const uint32_t h2 = sh.hist[4 * l + 2], h3 = sh.hist[4 * l + 3];
-      const uint32_t mine = h0 + h1 + h2 + h3;
-      uint32_t suffix = mine;  // sum over lanes >= l
+    // lane l owns bins 4l..4l+3; the lane whose bins hold the kk-th largest
+    // finds the digit, which every lane then reads from it
+    const uint4 h = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+    const uint32_t mine = (h.x + h.y) + (h.z + h.w);
+    uint32_t suffix = mine;  // sum over lanes >= l
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_down((int)suffix, o, kWave);
-        if (l + o < kWave) suffix += y;
-      }
-      const uint32_t higher = suffix - mine;  // keys in bins above lane l's
-      if (higher < kk && kk <= suffix) {
-        uint32_t acc = higher;
-        uint32_t digit = 4u * l;
-        const uint32_t hb[4] = {h0, h1, h2, h3};
-#pragma unroll
-        for (int b = 3; b >= 0; --b) {
-          if (acc + hb[b] >= kk) { digit = 4u * l + b; break; }
-          acc += hb[b];
-        }
-        sh.scal[0] = digit;
-        sh.scal[1] = acc;
-      }
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_down((int)suffix, o, kWave);
+      if (lane + o < kWave) suffix += y;
     }
-    __syncthreads();
-    const uint32_t digit = sh.scal[0], higher = sh.scal[1];
-    above += higher;
-    kk -= higher;
+    const uint32_t higher = suffix - mine;  // keys in bins above lane l's
+    const bool owner = higher < kk && kk <= suffix;
+    uint32_t acc = higher, digit = 4u * (uint32_t)lane;
+    const uint32_t hb[4] = {h.x, h.y, h.z, h.w};
+    bool found = false;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+      if (!found && acc + hb[b] >= kk) {
+        digit = 4u * (uint32_t)lane + (uint32_t)b;
+        found = true;
+      }
+      if (!found) acc += hb[b];
+    }
+    const int src_lane = __ffsll((unsigned long long)__ballot(owner)) - 1;
+    digit = (uint32_t)__shfl((int)digit, src_lane, kWave);
+    acc = (uint32_t)__shfl((int)acc, src_lane, kWave);
+    above += acc;
+    kk -= acc;
     prefix |= digit << shift;
     mask |= 255u << shift;
   }
