@@ -30,6 +30,11 @@ namespace {
 constexpr int C = kAttnChunk;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on this architecture (32-bit data format,
+// no swizzle, no index stride): loads past num_records return zeros.
+constexpr int kBufferFormat = 0x00020000;
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -113,10 +118,11 @@ struct RowSource {
 };
 
 // Three resident workgroups per compute unit (at most 168 VGPRs) where the
-// GQA group fits them without spills.
+// GQA group fits them without spills; two for the compact mode at D * GQ =
+// 1024 (measured slightly faster: no spill, more registers for the loads).
 template <int D, int GQ, int MODE>
 __global__ void __launch_bounds__(4 * kWave)
-__attribute__((amdgpu_waves_per_eu(D * GQ <= 1024 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu((MODE == kCompact ? D * GQ < 1024 : D * GQ <= 1024) ? 3 : 2)))
 attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* __restrict__ width,
                     int32_t q_heads, int32_t kv_heads, int32_t stride, int32_t n_chunks,
                     float scale, int64_t row0, int64_t rows, float* __restrict__ part_acc,
@@ -140,11 +146,13 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   const int64_t items = (int64_t)n_chunks * rows * kv_heads;
   const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact or cache rows
 
-  // Every load is unconditional: rows past a chunk's width read the chunk's
-  // last valid row (always in bounds); their scores are replaced by -inf and
-  // their weights p are 0, so they add nothing.  No load sits behind a branch.
-  // Prefetches are unconditional as well: an empty or out-of-range next item
-  // loads (and ignores) row 0 of the last item's chunk, which always exists.
+  // Every load is unconditional: rows past a chunk's width read zeros (compact
+  // mode, through the item's buffer resource) or the chunk's last valid row
+  // (cache and union modes, always in bounds); their scores are replaced by
+  // -inf and their weights p are 0, so they add nothing.  No load sits behind
+  // a branch.  Prefetches are unconditional as well: an empty or out-of-range
+  // next item reads nothing (compact: an empty resource) or row 0 of the last
+  // item's chunk, which always exists, and ignores it.
   auto chunk_rows = [&](const Item& x) -> int {  // rows of this chunk, 0 = no work
     const int32_t w = width[row0 + x.lrow];
     const int c0 = x.chunk * C;
@@ -168,7 +176,42 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   // K rows and the query heads of item x (q staged in LDS next to K, so the
   // score loop reads it with broadcast LDS loads instead of scalar loads
   // that would each wait on a cache round trip)
+  // Compact rows are read through a buffer resource per item that covers
+  // only the item's valid rows (the loads return raw 32-bit words, bit-cast
+  // to float): rows past the width read as zeros (their
+  // scores are replaced by -inf and their weights are 0), so the loads need
+  // no clamp and no 64-bit address arithmetic.  The item is uniform across
+  // the workgroup, so the descriptor is kept in scalar registers.
+  auto item_rsrc = [&](const float* compact, const Item& x, int cn_raw) {
+    const float* base =
+        compact + ((x.lrow * kv_heads + x.hk) * stride + (int64_t)x.chunk * C) * (int64_t)D;
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane(cn_raw * D * 4);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                             (short)0, bytes, kBufferFormat);
+  };
+  auto load_q = [&](const Item& x) {
+    const float* qg = q + ((row0 + x.lrow) * q_heads + (int64_t)x.hk * GQ) * D;
+#pragma unroll
+    for (int r = 0; r < QV4; ++r) {
+      const int e = tid + r * NT;
+      qst[r] = *reinterpret_cast<const float4*>(qg + 4 * (e < GQ * D / 4 ? e : 0));
+    }
+  };
   auto load_k = [&](const Item& x, int cn_raw, int ring_slot) {
+    if constexpr (MODE == kCompact) {
+      const auto rs = item_rsrc(src.k_compact, x, cn_raw);
+#pragma unroll
+      for (int r = 0; r < KV4; ++r) {  // float4 e of the item's rows is at byte 16e
+        const f32x4 v = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + r * NT) * 16, 0, 0));
+        kst[r] = make_float4(v.x, v.y, v.z, v.w);
+      }
+      load_q(x);
+      return;
+    }
     const int cn = cn_raw > 0 ? cn_raw : 1;
 #pragma unroll
     for (int r = 0; r < KV4; ++r) {
@@ -179,14 +222,26 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       kst[r] = *reinterpret_cast<const float4*>(
           row_ptr(src.k_compact, src.k_cache, x, ic, ring_slot) + 4 * c);
     }
-    const float* qg = q + ((row0 + x.lrow) * q_heads + (int64_t)x.hk * GQ) * D;
-#pragma unroll
-    for (int r = 0; r < QV4; ++r) {
-      const int e = tid + r * NT;
-      qst[r] = *reinterpret_cast<const float4*>(qg + 4 * (e < GQ * D / 4 ? e : 0));
-    }
+    load_q(x);
   };
   auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
+    if constexpr (MODE == kCompact) {
+      const auto rs = item_rsrc(src.v_compact, x, cn_raw);
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const int i = wave * KPW + j;
+        if constexpr (DPL == 2) {
+          const f32x2 v = __builtin_bit_cast(
+              f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (i * D + 2 * lane) * 4, 0, 0));
+          vreg[j][0] = v.x;
+          vreg[j][1] = v.y;
+        } else {
+          vreg[j][0] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rs, (i * D + lane) * 4, 0, 0));
+        }
+      }
+      return;
+    }
     const int cn = cn_raw > 0 ? cn_raw : 1;
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
