@@ -50,6 +50,7 @@ struct AttnCfg {
   static constexpr int DPL = D / kWave;  // output dims per lane
   static constexpr int KV4 = C * D / 4 / NT;  // K float4 per thread per chunk
   static constexpr int QV4 = (GQ * D / 4 + NT - 1) / NT;  // q float4 per thread per item
+  static constexpr int OV4 = QV4;                          // partial float4 per thread per item
   static constexpr int KFLOATS = C * KP;
   static constexpr int RFLOATS = NW * GQ * D;  // per-wavefront P.V partials, aliasing K
   static constexpr int SFLOATS = KFLOATS > RFLOATS ? KFLOATS : RFLOATS;
@@ -130,7 +131,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   using A = AttnCfg<D, GQ>;
   constexpr bool FUSED = MODE != kCompact;
   constexpr int NW = A::NW, NT = A::NT, KPW = A::KPW, KP = A::KP;
-  constexpr int DPL = A::DPL, KV4 = A::KV4, QV4 = A::QV4;
+  constexpr int DPL = A::DPL, KV4 = A::KV4, QV4 = A::QV4, OV4 = A::OV4;
   __shared__ float4 smem4[A::SFLOATS / 4];
   __shared__ float4 ql4[GQ * D / 4];          // the item's query heads
   __shared__ float4 ps4[GQ * C / 4];
@@ -313,7 +314,10 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     resolve_store(1);
     __syncthreads();
   }
+  // K before V here as in the loop: the wait for K at the top of an item can
+  // then leave V (issued after it) in flight on every path into the loop
   load_k(cur, cn, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_v(cur, cn, 0);
   while (it < items) {
     const int64_t it_next = it + gridDim.x;
@@ -357,12 +361,15 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       __builtin_amdgcn_sched_barrier(0);
       load_k(nxt, cn_next, rs_next);
       resolve_ids(nxt2, cn_next2);
+      __builtin_amdgcn_sched_barrier(0);  // issued before the score phase
 
       // scores on v_mfma_f32_16x16x4_f32: S[row 16w + 4lq + r][head li] in
       // sacc[r] (lane (li, lq) = lane % 16, lane / 16); k-step (c, e) covers
-      // dim 16c + 4lq + e in both operands; head columns past the group read
-      // zeros.  Two independent accumulators (even and odd e), added at the
-      // end.
+      // dim 16c + 4lq + e in both operands.  Head columns past the group
+      // repeat head 0: MFMA columns are independent, and those lanes' scores
+      // are never stored or exchanged (a masked operand would put a branch
+      // and a full LDS wait into every k-step).  Two independent accumulators
+      // (even and odd e), added at the end.
       const int li = lane & 15, lq = lane >> 4;
       const bool hcol = li < GQ;
       f32x4 sp[2];
@@ -371,8 +378,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const float4 a4 = smem4[((16 * wave + li) * KP + 16 * c + 4 * lq) / 4];
-        float4 b4 = ql4[((hcol ? li : 0) * D + 16 * c + 4 * lq) / 4];
-        if (!hcol) b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 b4 = ql4[((hcol ? li : 0) * D + 16 * c + 4 * lq) / 4];
         sp[0] = mfma4(a4.x, b4.x, sp[0]);
         sp[1] = mfma4(a4.y, b4.y, sp[1]);
         sp[0] = mfma4(a4.z, b4.z, sp[0]);
@@ -453,13 +459,28 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)tid * n_chunks) * 2) =
             make_float2(m, l);
       }
-      for (int o = tid; o < (cn > 0 ? GQ * D : 0); o += NT) {
-        const int h = o / D;
-        const int d = o - h * D;
-        float sum = smem[h * D + d];
+      // four consecutive outputs per thread and a fixed store count per item
+      // (a store loop of runtime length made the compiler wait for every
+      // outstanding load, the next item's V included, at the top of the item)
+      if (cn > 0) {
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) sum = sum + smem[(ww * GQ + h) * D + d];
-        part_acc[(slot0 + (int64_t)h * n_chunks) * D + d] = sum;
+        for (int r = 0; r < OV4; ++r) {
+          const int o4 = tid + r * NT;
+          if (o4 < GQ * D / 4) {
+            const int h = (4 * o4) / D;
+            const int d = 4 * o4 - h * D;
+            float4 sum = smem4[(h * D + d) / 4];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) {
+              const float4 t = smem4[((ww * GQ + h) * D + d) / 4];
+              sum.x = sum.x + t.x;
+              sum.y = sum.y + t.y;
+              sum.z = sum.z + t.z;
+              sum.w = sum.w + t.w;
+            }
+            *reinterpret_cast<float4*>(part_acc + (slot0 + (int64_t)h * n_chunks) * D + d) = sum;
+          }
+        }
       }
       resolve_store(FUSED ? (j + 2) % 3 : 0);  // visible after the next item's first barrier
     }
