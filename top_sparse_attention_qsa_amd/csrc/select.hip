@@ -275,18 +275,29 @@ __device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ s
     if ((fl >> e) & 1u) wlist[o++] = s0 + e;
   // (the list is written and read by this wavefront only)
 
-  // rounds of 64 scores: item i = 64r + lane is score i%16 of listed segment i/16
+  // rounds of 64 scores: item i = 64r + lane is score i%16 of listed segment
+  // i/16.  Every round's load is issued before any result is used (a load
+  // behind a branch, or used at once, would be waited for before the next
+  // one is issued: one memory round trip per round); items past the list
+  // read position 0 and are masked afterwards.
   const uint32_t items = nseg * kSegment;
   uint32_t key[kSegRounds], pos[kSegRounds];
   uint64_t hit[kSegRounds];
   uint32_t cnt = 0;
+  {
+    float sval[kSegRounds];
+    bool valid[kSegRounds];
 #pragma unroll
-  for (int r = 0; r < kSegRounds; ++r) {
-    const uint32_t i = 64u * r + (uint32_t)lane;
-    const bool in = i < items;
-    const uint32_t sg = wlist[in ? i / kSegment : 0];
-    pos[r] = sg * kSegment + (i % kSegment);
-    key[r] = (in && pos[r] < G) ? order_key(srow[pos[r]]) : 0u;
+    for (int r = 0; r < kSegRounds; ++r) {
+      const uint32_t i = 64u * r + (uint32_t)lane;
+      const bool in = i < items;
+      const uint32_t sg = wlist[in ? i / kSegment : 0];
+      pos[r] = sg * kSegment + (i % kSegment);
+      valid[r] = in && pos[r] < G;
+      sval[r] = srow[valid[r] ? pos[r] : 0u];
+    }
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r) key[r] = valid[r] ? order_key(sval[r]) : 0u;
   }
 #pragma unroll
   for (int r = 0; r < kSegRounds; ++r) {
