@@ -68,3 +68,13 @@ def test_full_decode_fused_equals_compact(full):
     torch.cuda.synchronize()
     assert torch.equal(ref[0], full.token_ids) and torch.equal(ref[1], full.width)
     assert torch.equal(ref[2], full.out) and torch.equal(ref[3], full.lse)
+
+
+def test_full_decode_dedup_equals_compact(full):
+    """The union gather on decode rows (one row per sequence, so each union is
+    the row's own groups) reads the same rows in the same order."""
+    ref = (full.token_ids.clone(), full.width.clone(), full.out.clone(), full.lse.clone())
+    full.decode(rows="dedup")
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], full.token_ids) and torch.equal(ref[1], full.width)
+    assert torch.equal(ref[2], full.out) and torch.equal(ref[3], full.lse)
