@@ -327,8 +327,13 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     const Item nxt2 = item_at(it_next2, raw2);
     const int cn_next2 = rows_at(it_next2, nxt2);
     const int rs_cur = FUSED ? j % 3 : 0, rs_next = FUSED ? (j + 1) % 3 : 0;
-    // An item with no rows (cn == 0) runs the same code on masked rows and
-    // skips its stores, so every prefetch is issued from one program point.
+    // A workgroup whose last item has no rows stops here (chunk-major items
+    // put the empty chunks of rows shorter than the longest possible width
+    // last, so this is the common case; the loads prefetched for the item are
+    // discarded).  Any other item with no rows runs the same code on masked
+    // rows and skips its stores, so every prefetch is issued from one program
+    // point.
+    if (cn == 0 && it_next >= items) break;
     {
       // stage this item's K in LDS (rows past the width hold a copy of the
       // last row -- their scores are replaced by -inf, so they are never
