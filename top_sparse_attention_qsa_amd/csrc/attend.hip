@@ -210,7 +210,6 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + r * NT) * 16, 0, 0));
         kst[r] = make_float4(v.x, v.y, v.z, v.w);
       }
-      load_q(x);
       return;
     }
     const int cn = cn_raw > 0 ? cn_raw : 1;
@@ -223,7 +222,6 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       kst[r] = *reinterpret_cast<const float4*>(
           row_ptr(src.k_compact, src.k_cache, x, ic, ring_slot) + 4 * c);
     }
-    load_q(x);
   };
   auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
     if constexpr (MODE == kCompact) {
@@ -258,35 +256,48 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       }
     }
   };
-  // Fused resolution of item x in three phases on wavefront 0, lane i = row i.
-  int32_t id_reg = -1, slot_reg = 0;
+  // Fused resolution of item x in three phases on wavefront 0, lane i = row i:
+  // IDs loaded (before the next item's K loads, so that waiting for them
+  // does not wait for K), the slot map read (its value checked only when the
+  // slots are stored, so the load is not waited for at once), and the slots
+  // written to the LDS ring at the end of the item.
+  int32_t id_reg = -1, len_reg = 0, sl_raw = 0;
+  int64_t soff_reg = 0;
+  bool id_ok = false;
   auto resolve_ids = [&](const Item& x, int cn_x) {
     if constexpr (FUSED) {
       if (wave == 0) {
         const int64_t row = MODE == kUnion ? x.lrow : row0 + x.lrow;
         id_reg = lane < cn_x ? src.token_ids[row * stride + (int64_t)x.chunk * C + lane] : -1;
+        if constexpr (MODE == kFused) {
+          const int32_t b = (int32_t)row / src.queries;  // rows fit in 32 bits (validated)
+          len_reg = src.seq_len[b];
+          soff_reg = src.slot_off[b];
+        }
       }
     }
   };
   auto resolve_slots = [&](const Item& x, int cn_x) {
     if constexpr (FUSED) {
       if (wave == 0 && MODE == kUnion) {
-        slot_reg = lane < cn_x ? ((id_reg >= 0 && (int64_t)id_reg < src.kv_slots) ? id_reg : -1) : 0;
+        id_ok = lane < cn_x && id_reg >= 0;
+        sl_raw = id_reg;
       } else if (wave == 0) {
-        const int32_t row = (int32_t)(row0 + x.lrow);  // rows fit in 32 bits (validated)
+        const int32_t row = (int32_t)(row0 + x.lrow);
         const int32_t b = row / src.queries;
-        const int64_t n = (int64_t)src.seq_len[b] - src.queries + 1 + (row - b * src.queries);
-        slot_reg = lane < cn_x ? -1 : 0;
-        if (lane < cn_x && id_reg >= 0 && (int64_t)id_reg < n) {
-          const int32_t sl = src.slot_map[src.slot_off[b] + id_reg];
-          slot_reg = (sl >= 0 && (int64_t)sl < src.kv_slots) ? sl : -1;
-        }
+        const int64_t n = (int64_t)len_reg - src.queries + 1 + (row - b * src.queries);
+        id_ok = lane < cn_x && id_reg >= 0 && (int64_t)id_reg < n;
+        if (id_ok) sl_raw = src.slot_map[soff_reg + id_reg];
       }
     }
   };
-  auto resolve_store = [&](int ring_slot) {
+  // rows past the width get slot 0 (a row that exists), invalid IDs or slots -1
+  auto resolve_store = [&](int ring_slot, int cn_x) {
     if constexpr (FUSED) {
-      if (wave == 0) ring[ring_slot][lane] = slot_reg;
+      if (wave == 0)
+        ring[ring_slot][lane] =
+            lane < cn_x ? ((id_ok && sl_raw >= 0 && (int64_t)sl_raw < src.kv_slots) ? sl_raw : -1)
+                        : 0;
     }
   };
 
@@ -308,15 +319,18 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     const Item x1 = item_at(it + gridDim.x, raw1);
     resolve_ids(cur, cn);
     resolve_slots(cur, cn);
-    resolve_store(0);
+    resolve_store(0, cn);
     resolve_ids(x1, rows_at(it + gridDim.x, x1));
     resolve_slots(x1, rows_at(it + gridDim.x, x1));
-    resolve_store(1);
+    resolve_store(1, rows_at(it + gridDim.x, x1));
     __syncthreads();
   }
-  // K before V here as in the loop: the wait for K at the top of an item can
-  // then leave V (issued after it) in flight on every path into the loop
+  // K, then q, then V here as in the loop: the wait for K and q at the top of
+  // an item can then leave V (issued after them) in flight on every path into
+  // the loop
   load_k(cur, cn, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_q(cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, cn, 0);
   while (it < items) {
@@ -354,18 +368,22 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         }
         smem4[(i * KP) / 4 + c] = kv;
       }
+      // (unconditional when the threads cover q exactly: a store behind a
+      // branch leaves the q load possibly pending on the other path, and the
+      // next write to its registers would wait for V loads issued after it)
 #pragma unroll
       for (int r = 0; r < QV4; ++r) {
         const int e = tid + r * NT;
-        if (e < GQ * D / 4) ql4[e] = qst[r];
+        if ((GQ * D / 4) % NT == 0 || e < GQ * D / 4) ql4[e] = qst[r];
       }
       __syncthreads();
       // next item's K streams in under this item; the scheduling barriers keep
       // the compiler from hoisting it (or V below) above the last use of the
       // registers it refills, which would double the register footprint
       __builtin_amdgcn_sched_barrier(0);
-      load_k(nxt, cn_next, rs_next);
       resolve_ids(nxt2, cn_next2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(nxt, cn_next, rs_next);
       __builtin_amdgcn_sched_barrier(0);  // issued before the score phase
 
       // scores on v_mfma_f32_16x16x4_f32: S[row 16w + 4lq + r][head li] in
@@ -447,7 +465,9 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_v(nxt, cn_next, rs_next);  // next item's V streams in under the rest
+      load_q(nxt);  // the next item's query heads, then its V, stream in under the rest
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(nxt, cn_next, rs_next);
 
       // combine the wavefronts' partial sums in wavefront order
 #pragma unroll
@@ -487,7 +507,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
           }
         }
       }
-      resolve_store(FUSED ? (j + 2) % 3 : 0);  // visible after the next item's first barrier
+      resolve_store(FUSED ? (j + 2) % 3 : 0, cn_next2);  // visible after the next item's first barrier
     }
     it = it_next;
     raw1 = raw2;
