@@ -37,29 +37,36 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
   const int tid = (int)threadIdx.x;
   const int64_t lrow = blockIdx.y;
   const int64_t row = row0 + lrow;
-  const int32_t w = width[row];
   const int32_t i0 = (int32_t)blockIdx.x * kGatherTokens;
+  // The width, the token IDs (read speculatively, clamped to the row), the
+  // sequence length and the slot-map offset do not depend on each other:
+  // they are loaded together, then the slot map -- two dependent memory
+  // round trips before the copy instead of four.
+  const int32_t w = width[row];
+  const int32_t b = (int32_t)(row / queries);
+  const int32_t i = i0 + tid;
+  int32_t id = -1, len = 0;
+  int64_t soff = 0;
+  if (tid < kGatherTokens) {
+    id = token_ids[row * stride + (i < stride ? i : stride - 1)];
+    len = seq_len[b];
+    soff = slot_off[b];
+  }
   if (w <= 0 || w > stride - 1 || i0 >= w) return;  // widths above 4k+3 are invalid
   if (tid < kGatherTokens) {
-    const int32_t i = i0 + tid;
     int32_t slot = -2;  // -2: past the width, nothing to copy
     if (i < w) {
-      const int32_t b = (int32_t)(row / queries);
-      const int64_t n = (int64_t)seq_len[b] - queries + 1 + (row - (int64_t)b * queries);
-      const int32_t id = token_ids[row * stride + i];
+      const int64_t n = (int64_t)len - queries + 1 + (row - (int64_t)b * queries);
       slot = -1;
       if (id >= 0 && (int64_t)id < n) {
-        const int32_t s = slot_map[slot_off[b] + id];
-        if (s >= 0 && (int64_t)s < kv_slots) slot = s;
+        const int32_t sl = slot_map[soff + id];
+        if (sl >= 0 && (int64_t)sl < kv_slots) slot = sl;
       }
       if (phys_slots) phys_slots[row * stride + i] = slot;
     }
     slot_sh[tid] = slot;
   }
   __syncthreads();
-  // All loads of a thread are issued before any store (slots that are out of
-  // range or past the width read slot 0 and are masked afterwards), so the
-  // copy is one memory round trip per workgroup, not one per float4.
   // All loads of a pass are issued before any store (slots that are out of
   // range or past the width read slot 0, which exists because kv_slots >= 1,
   // and are masked afterwards), so each pass costs one memory round trip.
