@@ -72,7 +72,7 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
   // and are masked afterwards), so each pass costs one memory round trip.
   const float nan = __int_as_float(0x7fc00000);
   const int total = kGatherTokens * row_f4;
-  constexpr int kPer = 8;  // float4 per thread per pass
+  constexpr int kPer = 4;  // float4 per thread per pass (one pass for H_kv x D = 512)
   for (int base = 0; base < total; base += kPer * 256) {
     float4 kv[kPer], vv[kPer];
 #pragma unroll
