@@ -257,6 +257,59 @@ def chunk_leg(seed, steps):
             "rows": rows, "steps": steps, **res}
 
 
+def time_calls(fn, reps):
+    """Mean milliseconds of fn() over reps calls, bracketed by synchronizations."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def pool_leg(case, raw_keys, reps=5):
+    """Group pooling of the decode batch on the GPU: 32 x 262,144 raw index
+    keys of 128 floats (4 GiB) into the tiled pooled keys (1 GiB); the result
+    must equal the pooled keys the inputs were built with."""
+    import torch
+    import top_sparse_attention_qsa_amd as qsa
+    out = torch.empty_like(case.pooled)
+    ms = time_calls(lambda: qsa.qsa_pool_groups(case.shape, raw_keys, case.raw_off, case.seq_len,
+                                                None, out, case.pooled_off), reps)
+    assert torch.equal(out, case.pooled), "pooling differs from the input build"
+    s = case.spec
+    groups = sum(n // 4 for n in s.seq_lens)
+    nbytes = groups * s.d_i * 4 * 5  # four raw rows read, one pooled row written
+    del out
+    return {"ms": ms, "algorithmic_bytes": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9,
+            "note": "qsa_pool_groups over every complete group of the decode batch"}
+
+
+def dense_leg(case, reps=20):
+    """The bounded dense row on the GPU (every visible token, no selection)
+    at its largest width: the decode batch's 32 rows cut to 2,051 visible
+    tokens, through the same gather, attention and merge."""
+    import torch
+    import top_sparse_attention_qsa_amd as qsa
+    s = case.spec
+    seq = torch.full_like(case.seq_len, 4 * s.budget + 3)
+    ids = torch.empty_like(case.token_ids)
+    width = torch.empty_like(case.width)
+    out = torch.empty_like(case.out)
+    lse = torch.empty_like(case.lse)
+    ms = time_calls(lambda: qsa.qsa_dense_attend(case.shape, seq, case.slot_map, case.slot_off,
+                                                 case.k_cache, case.v_cache, case.q, case.scale,
+                                                 ids, width, out, lse, case.workspace), reps)
+    assert int(width.min()) == 4 * s.budget + 3 and int(width.max()) == 4 * s.budget + 3
+    return {"ms": ms, "rows_per_s": s.rows / (ms * 1e-3), "width": 4 * s.budget + 3,
+            "note": "qsa_dense_attend, 32 rows of 2,051 visible tokens each"}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -283,7 +336,7 @@ def copy_calibration(gib=1.0, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -317,6 +370,8 @@ def main():
     data = inputs.make(spec, seed=args.seed, device="cuda")
     case = harness.GpuCase(data)
     rows = spec.rows
+    print("[bench] pooling leg", file=sys.stderr, flush=True)
+    pool = pool_leg(case, data["raw_keys"])
     keep_raw = not args.no_cpu_baseline
     if not keep_raw:
         data["raw_keys"] = None
@@ -444,6 +499,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    print("[bench] dense leg", file=sys.stderr, flush=True)
+    result["pool"] = pool
+    result["dense"] = dense_leg(case)
     if not args.no_chunk:
         print("[bench] chunk leg", file=sys.stderr, flush=True)
         result["chunk"] = chunk_leg(args.seed, steps=5)

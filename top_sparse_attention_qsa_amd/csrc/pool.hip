@@ -9,9 +9,12 @@
 // same bits (AFN-017 "Top-k chooses the set; time chooses the order", capsule
 // evidence: full-raw/incremental identity).
 //
-// A thread owns one float4 of one group: it reads the four raw rows (the
-// reads of consecutive threads are contiguous) and writes the 16-byte slot
-// of the tiled layout.
+// A thread owns one float4 of one group: it reads the four raw rows and
+// writes the 16-byte slot of the tiled layout.  Lanes are laid out as
+// kGroups consecutive groups by dimension chunk, so that each load of a
+// wavefront reads 128-byte runs of raw rows and each store writes 128-byte
+// runs of the tiled layout (consecutive groups of one chunk are adjacent
+// there).
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -23,6 +26,7 @@ pool_kernel(const float* __restrict__ raw, const int64_t* __restrict__ raw_off,
             const int32_t* __restrict__ seq_len, const int32_t* __restrict__ first_group,
             float* __restrict__ pooled, const int64_t* __restrict__ pooled_off, int64_t g_max) {
   constexpr int NC = DI / 4;
+  constexpr int kGroups = 8;  // divides every max_groups (a multiple of 64)
   const int b = (int)blockIdx.y;
   const int64_t n = seq_len[b];
   int64_t G = n > 0 ? n / 4 : 0;
@@ -30,8 +34,10 @@ pool_kernel(const float* __restrict__ raw, const int64_t* __restrict__ raw_off,
   int64_t g_from = first_group ? (int64_t)first_group[b] : 0;
   if (g_from < 0) g_from = 0;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t g = e / NC;
-  const int c = (int)(e - g * NC);
+  const int64_t blk = e / (kGroups * NC);
+  const int u = (int)(e - blk * (kGroups * NC));
+  const int c = u / kGroups;
+  const int64_t g = blk * kGroups + (u - c * kGroups);
   if (g < g_from || g >= G) return;
   const float* r = raw + (raw_off[b] + 4 * g) * DI + 4 * c;
   const float4 r0 = *reinterpret_cast<const float4*>(r);
