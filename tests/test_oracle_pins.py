@@ -132,7 +132,7 @@ def rank_count_select(scores, k):
 
 def test_select_matches_rank_count_bruteforce():
     rng = np.random.default_rng(51)
-    for trial in range(3000):
+    for trial in range(10000):
         g = int(rng.integers(0, 65))
         k = int(rng.integers(1, 17))
         levels = int(rng.integers(1, 6))
