@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "QSA decode queries/sec at 262,144 visible tokens; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 COUNTERS = os.path.join(ROOT, "profiles", "score_32x262144_counters.json")
 
 
@@ -251,10 +252,35 @@ def chunk_leg(seed, steps):
     res["fused"]["kv_rows_copied"] = 0
     for m in ("compact", "dedup"):
         res[m]["kv_copy_bytes"] = 2 * 2 * kv_row * res[m]["kv_rows_copied"]  # K+V, read+write
+    res["score_mfma"] = chunk_score_roofline(case, steps)
     return {"workload": "causal chunks: 8 sequences, lengths U[2,051, 262,144] (seeded), 256 "
                         "queries each, budget 512, indexer 16 x 128, attention 32 q / 4 KV x "
                         "128, identity slot maps, 256 rows in flight",
             "rows": rows, "steps": steps, **res}
+
+
+def chunk_score_roofline(case, reps):
+    """The chunk scoring kernel alone (fp32 MFMA, every row of the chunk
+    workload): algorithmic flops = sum over rows of 2 x H_I x D_I x G_row,
+    against MI355X's dense fp32 matrix peak."""
+    import torch
+    import top_sparse_attention_qsa_amd as qsa
+    from tests import inputs
+    s = case.spec
+    sh = case.shape
+    approx = torch.empty((s.rows, sh.max_groups), device="cuda")
+    bound = torch.empty_like(approx)
+    ms = time_calls(lambda: qsa.qsa_score_groups_chunk(sh, case.index_q, case.pooled,
+                                                       case.pooled_off, case.seq_len, approx,
+                                                       bound), reps)
+    groups = sum(inputs.row_tokens(s, r) // 4 for r in range(s.rows))
+    flop = 2.0 * s.h_i * s.d_i * groups
+    achieved = flop / (ms * 1e-3) / 1e12
+    del approx, bound
+    return {"kernel": f"chunk_score_kernel<{s.h_i},{s.d_i}>", "bound": "mfma", "ms": ms,
+            "algorithmic_flop": flop, "achieved": achieved, "peak": MFMA_FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / MFMA_FP32_PEAK_TFLOPS,
+            "note": "qsa_score_groups_chunk over every row, v_mfma_f32_16x16x4_f32"}
 
 
 def time_calls(fn, reps):

@@ -128,6 +128,12 @@ typedef struct qsa_bytes {
  * k_compact,  [rows][H_kv][4k+4][D] f32: each KV head's selected rows of a
  * v_compact   query row are contiguous; positions at or past width untouched.
  * q           [rows][H_q][D] f32.  out [rows][H_q][D] f32; lse [rows][H_q].
+ *
+ * Buffers moved with 16-byte vector accesses must be 16-byte aligned:
+ * raw_keys, pooled, scores, token_ids, k_cache, v_cache, k_compact,
+ * v_compact, q, out, the workspace, and index_q wherever chunk scoring may
+ * run (qsa_score_groups_chunk and the qsa_decode entry points).  A
+ * misaligned pointer returns QSA_ERR_SHAPE before anything is enqueued.
  */
 
 /* Workspace bytes qsa_decode needs for this shape (also enough for

@@ -126,6 +126,11 @@ def test_null_pointers_and_small_workspace_rejected():
     # misaligned device pointers are refused, not dereferenced
     odd = ctypes.c_void_p(258)
     assert L.qsa_score_groups(ctypes.byref(s), p, odd, p, p, p, None) == qsa.QSA_ERR_SHAPE
+    chunk = shape(queries=16)
+    assert L.qsa_score_groups_chunk(ctypes.byref(chunk), odd, p, p, p, p, p, None) == \
+        qsa.QSA_ERR_SHAPE
+    assert L.qsa_decode(ctypes.byref(s), odd, *([p] * 8), ctypes.c_float(0.1), p, p, p, None, p,
+                        ctypes.c_size_t(1 << 40), None, None) == qsa.QSA_ERR_SHAPE
     assert L.qsa_accounting(ctypes.byref(s), 10, None) == qsa.QSA_ERR_NULL
     assert L.qsa_timer_create(0, 1, None) == qsa.QSA_ERR_NULL
     h = ctypes.c_void_p()

@@ -187,7 +187,7 @@ int qsa_score_groups_chunk(const qsa_shape* s, const float* index_q, const float
   int rc = validate(s, kNeedIndex);
   if (rc != QSA_OK) return rc;
   if (!index_q || !pooled || !pooled_off || !seq_len || !approx || !bound) return QSA_ERR_NULL;
-  if (!aligned16(pooled)) return QSA_ERR_SHAPE;
+  if (!aligned16(index_q) || !aligned16(pooled)) return QSA_ERR_SHAPE;
   if (!chunk_supported(s->index_heads, s->queries, row_count(s))) return QSA_ERR_UNSUPPORTED;
   ChunkArgs a{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, 0, row_count(s),
               approx, bound, nullptr, nullptr};
@@ -381,8 +381,8 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
   if (!index_q || !pooled || !pooled_off || !seq_len || !slot_map || !slot_off || !k_cache ||
       !v_cache || !q || !token_ids || !width || !out || !ws)
     return QSA_ERR_NULL;
-  if (!aligned16(pooled) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) ||
-      !aligned16(out) || !aligned16(token_ids) || !aligned16(ws))
+  if (!aligned16(index_q) || !aligned16(pooled) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(q) || !aligned16(out) || !aligned16(token_ids) || !aligned16(ws))
     return QSA_ERR_SHAPE;
   const Layout L = layout(s);
   if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;

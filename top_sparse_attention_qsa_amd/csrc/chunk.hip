@@ -23,9 +23,14 @@
 //
 // Mapping: a workgroup owns 4 M-tiles of 16 (row, head) pairs (16/H_I rows
 // each) and 4 wavefronts; each wavefront owns one 64-group pooled-key tile
-// (4 N-subtiles of 16 groups).  A fragments are staged in LDS once per
-// workgroup; B fragments are single dword loads that read 256 contiguous
-// bytes of the tiled layout per wavefront.
+// (4 N-subtiles of 16 groups).  The contraction over d may take the dimensions
+// in any order (the bound does not depend on it), so k-slot kk of k-step
+// 4q + i carries dimension 16q + 4kk + i: a lane then reads the B operands of
+// four consecutive k-steps as one float4 of its group's key (dimension chunk
+// 4q + kk of the tiled layout), and 16 lanes read 256 contiguous bytes.  A
+// fragments are staged in LDS once per workgroup in the same order, one
+// float4 per (quad, M-tile, lane).  The B loads of quad q + 1 are in flight
+// while quad q runs on MFMA.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -33,8 +38,13 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// At least three wavefronts per SIMD: without the register limit this sets,
+// the compiler takes enough registers that only two fit, and the MFMA pipes
+// idle while they wait for B (measured 25% slower at 16 heads x 128).
+// Smaller index shapes hold more rows per workgroup and keep the default.
 template <int HI, int DI>
 __global__ void __launch_bounds__(4 * kWave)
+__attribute__((amdgpu_waves_per_eu(HI * DI >= 512 ? 3 : 2)))
 chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled,
                    const int64_t* __restrict__ pooled_off, const int32_t* __restrict__ seq_len,
                    int32_t queries, int64_t g_max, int64_t row0, float* __restrict__ approx,
@@ -42,8 +52,8 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
                    uint32_t* __restrict__ lo_maxima) {
   constexpr int RPM = 16 / HI;    // query rows per M-tile
   constexpr int RB = 4 * RPM;     // query rows per workgroup
-  constexpr int NK = DI / 4;      // k-steps
-  __shared__ float qa[NK * 4 * kWave];  // A fragments [k-step][M-tile][lane]
+  constexpr int NQ = DI / 16;     // quads of four k-steps
+  __shared__ f32x4 qa[NQ * 4 * kWave];  // A fragments [quad][M-tile][lane], 4 k-steps each
   __shared__ float hnorm[RB * HI];      // |q_(row, head)|
   __shared__ float qnorm[RB];           // sum over heads of |q_h| per row
 
@@ -54,20 +64,37 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   const int64_t grow0 = row0 + lrow0;
   const int b = (int)(grow0 / queries);            // all RB rows share this sequence
 
-  // stage A fragments: A[i][k] of M-tile m, k-step c = q[row][head][4c + k]
-  // with M-row i -> (row m*RPM + i/HI, head i%HI), i = lane%16, k = lane/16
-  for (int e = tid; e < NK * 4 * kWave; e += 4 * kWave) {
-    const int l = e & (kWave - 1);
-    const int m = (e / kWave) & 3;
-    const int c = e / (4 * kWave);
-    const int i = l & 15;
-    const int r = m * RPM + i / HI;
-    qa[e] = index_q[((grow0 + r) * HI + (i % HI)) * DI + 4 * c + (l >> 4)];
+  // stage A fragments: A[i][kk] of M-tile m, k-step 4q + s = q[row][head][16q + 4kk + s]
+  // with M-row i -> (row m*RPM + i/HI, head i%HI), i = lane%16, kk = lane/16.
+  // Each thread moves NQ float4s (four consecutive dimensions each), all
+  // loads issued before the first store.
+  {
+    f32x4 st[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int f = tid + n * 4 * kWave;  // (quad * 4 + M-tile) * 64 + lane
+      const int l = f & (kWave - 1);
+      const int m = (f >> 6) & 3;
+      const int i = l & 15;
+      const int r = m * RPM + i / HI;
+      st[n] = *reinterpret_cast<const f32x4*>(
+          index_q + ((grow0 + r) * HI + (i % HI)) * DI + 16 * (f >> 8) + 4 * (l >> 4));
+    }
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) qa[tid + n * 4 * kWave] = st[n];
   }
-  if (tid < RB * HI) {  // RB * HI == 64: one (row, head) per lane of wavefront 0
-    const float* qh = index_q + (grow0 * HI + tid) * DI;
+  __syncthreads();
+  if (tid < RB * HI) {  // (row, head) pair tid = M-tile tid/16, M-row tid%16 (RB * HI == 64)
     float ss = 0.0f;
-    for (int d = 0; d < DI; ++d) ss = __builtin_fmaf(qh[d], qh[d], ss);
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const f32x4 v = qa[(q * 4 + (tid >> 4)) * kWave + kk * 16 + (tid & 15)];
+        ss = __builtin_fmaf(v.x, v.x, ss);
+        ss = __builtin_fmaf(v.y, v.y, ss);
+        ss = __builtin_fmaf(v.z, v.z, ss);
+        ss = __builtin_fmaf(v.w, v.w, ss);
+      }
     hnorm[tid] = sqrtf(ss);
   }
   __syncthreads();
@@ -97,29 +124,47 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ksq[4] = {0.f, 0.f, 0.f, 0.f};
-  // B[k][j] of N-subtile t, k-step c = key[group 16t + j][4c + k], j = lane%16, k = lane/16
-  const int boff = (lane & 15) * 4 + (lane >> 4);
-  float bcur[4], bnext[4];
+  // lane (kk, j) of N-subtile t, quad q reads dimensions 16q + 4kk .. +3 of group 16t + j
+  const float* __restrict__ kl = kt + (lane >> 4) * 256 + (lane & 15) * 4;
+  auto load_quad = [&](f32x4 (&dst)[4], int q) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) bcur[t] = kt[t * 64 + boff];
-#pragma unroll 2
-  for (int c = 0; c < NK; ++c) {
-    if (c + 1 < NK) {
+    for (int t = 0; t < 4; ++t) dst[t] = *reinterpret_cast<const f32x4*>(kl + q * 1024 + t * 64);
+  };
+  auto run_quad = [&](const f32x4 (&bv)[4], int q) {
+    f32x4 a[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bnext[t] = kt[(c + 1) * 256 + t * 64 + boff];
-    }
-    float a[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = qa[(c * 4 + m) * kWave + lane];
+    for (int m = 0; m < 4; ++m) a[m] = qa[(q * 4 + m) * kWave + lane];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      ksq[t] = __builtin_fmaf(bcur[t], bcur[t], ksq[t]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bcur[t], acc[m][t], 0, 0, 0);
+      float kk = ksq[t];
+      kk = __builtin_fmaf(bv[t].x, bv[t].x, kk);
+      kk = __builtin_fmaf(bv[t].y, bv[t].y, kk);
+      kk = __builtin_fmaf(bv[t].z, bv[t].z, kk);
+      kk = __builtin_fmaf(bv[t].w, bv[t].w, kk);
+      ksq[t] = kk;
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bcur[t] = bnext[t];
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m][s], bv[t][s], acc[m][t], 0, 0, 0);
+  };
+  // two-deep ring over quads (NQ is even); the last refill re-reads the last
+  // quad instead of being conditional, so every wait is for the older quad only
+  f32x4 b0[4], b1[4];
+  load_quad(b0, 0);
+#pragma unroll 1
+  for (int q = 0; q < NQ; q += 2) {
+    load_quad(b1, q + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    run_quad(b0, q);
+    __builtin_amdgcn_sched_barrier(0);
+    load_quad(b0, q + 2 < NQ ? q + 2 : NQ - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    run_quad(b1, q + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   constexpr float u = 5.9604644775390625e-8f;  // 2^-24
