@@ -370,6 +370,8 @@ def main():
                     help="skip the causal-chunk leg (compact vs union gather vs fused)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter scale factor)")
+    ap.add_argument("--chunk-only", action="store_true",
+                    help="only run the causal-chunk leg and print its JSON (for profiling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -388,6 +390,9 @@ def main():
     qsa.lib()  # fails loudly if the HIP library is missing
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.chunk_only:
+        print(json.dumps({"chunk": chunk_leg(args.seed, steps=5)}))
         return
 
     spec = inputs.spec("decode_32x262144")
