@@ -22,6 +22,8 @@
 // partial sums are then added in wavefront order.  The chunk's accumulation
 // order is therefore fixed by the chunk alone.  merge_kernel: four
 // wavefronts per (query head, row).
+#include <atomic>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -630,7 +632,10 @@ namespace {
 template <int D, int GQ, int MODE>
 hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
   using A = AttnCfg<D, GQ>;
-  static int per_cu = 0;  // resident workgroups per compute unit for this instance
+  // resident workgroups per compute unit for this instance; concurrent first
+  // calls may both query it and store the same value
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attend_chunk_kernel<D, GQ, MODE>, A::NT,
@@ -638,6 +643,7 @@ hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
         n < 1)
       n = 1;
     per_cu = n;
+    per_cu_cache.store(n, std::memory_order_relaxed);
   }
   const int64_t items = (int64_t)a.n_chunks * a.rows * a.kv_heads;
   const int64_t slots = (int64_t)device_cus() * per_cu;
