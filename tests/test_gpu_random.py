@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import top_sparse_attention_qsa_amd as qsa
 from tests import harness, inputs
 from tests.test_gpu_parity import check_rows
 
@@ -65,3 +66,70 @@ def test_random_shape_matches_oracle_and_variants_agree(i):
             assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
                                b.view(torch.int32) if b.dtype == torch.float32 else b), \
                 (spec.name, rows)
+
+
+def bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("i", range(0, CASES, 2))
+def test_random_shape_step_by_step(i):
+    """The per-step entry points on the same random shapes: scores bit-exact
+    against the oracle; select + emit give the decode's IDs and widths (for
+    causal-chunk rows that is the exact selection against the certified one);
+    the gather copies the oracle's rows bit for bit; the standalone attention
+    equals the decode's output; NaN in every unselected cache row changes
+    nothing."""
+    import oracle
+    spec = random_spec(i)
+    print(f"case {i}: {spec}", flush=True)
+    data = inputs.make(spec, seed=100 + i, device="cpu")
+    case = harness.GpuCase(data)
+    case.decode()
+    torch.cuda.synchronize()
+    sh = case.shape
+    s = spec
+
+    scores = torch.full((s.rows, sh.max_groups), -1.0, device="cuda")
+    qsa.qsa_score_groups(sh, case.index_q, case.pooled, case.pooled_off, case.seq_len, scores)
+    bitmap = torch.full((s.rows, sh.max_groups // 32), -1, dtype=torch.int32, device="cuda")
+    qsa.qsa_select_topk(sh, scores, case.seq_len, bitmap, case.workspace)
+    ids = torch.empty_like(case.token_ids)
+    width = torch.empty_like(case.width)
+    qsa.qsa_emit_chronological(sh, bitmap, case.seq_len, ids, width)
+    assert torch.equal(ids, case.token_ids) and torch.equal(width, case.width)
+
+    kc = torch.full((s.rows, s.h_kv, sh.token_stride, s.d), 7.0, device="cuda")
+    vc = torch.full_like(kc, 7.0)
+    qsa.qsa_resolve_gather(sh, case.token_ids, case.width, case.seq_len, case.slot_map,
+                           case.slot_off, case.k_cache, case.v_cache, kc, vc)
+    out = torch.empty_like(case.out)
+    lse = torch.empty_like(case.lse)
+    qsa.qsa_online_attend(sh, case.q, kc, vc, case.width, case.scale, out, lse, case.workspace)
+    assert torch.equal(out, case.out) and torch.equal(lse, case.lse)
+
+    got_scores = scores.cpu().numpy()
+    kc, vc = kc.cpu().numpy(), vc.cpu().numpy()
+    keep = torch.zeros(data["kv_slots"], dtype=torch.bool)
+    for r in range(s.rows):
+        exp = harness.oracle_row(data, r, exact=False)
+        n = exp["n"]
+        b = r // s.queries
+        off = int(data["raw_off"][b])
+        want = oracle.score(data["index_q"][r].numpy(),
+                            oracle.pool_full(data["raw_keys"][off:off + n].numpy()))
+        assert np.array_equal(bits(got_scores[r, :len(want)]), bits(want)), (s.name, r)
+        w = len(exp["ids"])
+        kx = np.ascontiguousarray(kc[r, :, :w].transpose(1, 0, 2))
+        vx = np.ascontiguousarray(vc[r, :, :w].transpose(1, 0, 2))
+        assert kx.tobytes() == exp["kx"].tobytes() and vx.tobytes() == exp["vx"].tobytes()
+        keep[torch.as_tensor(exp["slots"], dtype=torch.int64)] = True
+
+    poisoned = harness.GpuCase(data)
+    keep = keep.cuda()
+    poisoned.k_cache[~keep] = float("nan")
+    poisoned.v_cache[~keep] = float("nan")
+    poisoned.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(poisoned.token_ids, case.token_ids)
+    assert torch.equal(poisoned.out.view(torch.int32), case.out.view(torch.int32))
