@@ -3,8 +3,9 @@ budget, key distribution, slot map, batch of sequence lengths (edge lengths
 around 0-5 and the budget, and random lengths up to 80,000 tokens) and, for
 index shapes the chunk scoring covers, causal chunk rows.  Every row must
 match the oracle (selected IDs, widths bit-exact; attention within 2e-6 of
-the exact attention over the oracle's rows), and the fused and union
-variants must equal the compact one bit for bit.
+the exact attention over the oracle's rows), the fused and union variants
+must equal the compact one bit for bit, and the bounded dense row must equal
+the sparse one wherever the row fits the budget.
 
 Sources: AFN-017 "Top-k chooses the set; time chooses the order" and AFN-016
 "A sparse mask is not sparse attention".
@@ -59,6 +60,23 @@ def test_random_shape_matches_oracle_and_variants_agree(i):
     case.decode()
     check_rows(case)
     ref = case.results()
+    # the bounded dense row: the same row as the sparse one at or below the
+    # budget (N <= 4k+3), refused above it
+    ids = torch.empty_like(case.token_ids)
+    width = torch.empty_like(case.width)
+    out = torch.empty_like(case.out)
+    lse = torch.empty_like(case.lse)
+    qsa.qsa_dense_attend(case.shape, case.seq_len, case.slot_map, case.slot_off, case.k_cache,
+                         case.v_cache, case.q, case.scale, ids, width, out, lse, case.workspace)
+    torch.cuda.synchronize()
+    for r in range(spec.rows):
+        n = inputs.row_tokens(spec, r)
+        if n <= 4 * spec.budget + 3:
+            assert int(width[r]) == n and torch.equal(ids[r], ref[0][r]), (spec.name, r)
+            assert torch.equal(out[r].view(torch.int32), ref[2][r].view(torch.int32))
+            assert torch.equal(lse[r].view(torch.int32), ref[3][r].view(torch.int32))
+        else:
+            assert int(width[r]) == -1 and torch.isnan(out[r]).all(), (spec.name, r)
     for rows in ("fused", "dedup"):
         case.decode(rows=rows)
         torch.cuda.synchronize()
