@@ -151,3 +151,50 @@ def test_random_shape_step_by_step(i):
     torch.cuda.synchronize()
     assert torch.equal(poisoned.token_ids, case.token_ids)
     assert torch.equal(poisoned.out.view(torch.int32), case.out.view(torch.int32))
+
+
+def untile(pooled_flat, off, g, d_i):
+    """Tiled pooled-key buffer of one sequence -> plain [G][D_I] (host)."""
+    tiles = (g + 63) // 64
+    t = pooled_flat[off:off + tiles * 64 * d_i].view(tiles, d_i // 4, 64, 4)
+    return t.permute(0, 2, 1, 3).reshape(tiles * 64, d_i)[:g].cpu().numpy()
+
+
+@pytest.mark.parametrize("i", range(1, CASES, 2))
+def test_random_shape_pooling(i):
+    """Group pooling on the random shapes: every sequence's pooled keys are the
+    oracle's bit for bit, and pooling in random increments (each call pools
+    only the groups completed since the previous one, every sequence on its
+    own schedule) gives the same bits as pooling the whole history."""
+    import oracle
+    spec = random_spec(i)
+    print(f"case {i}: {spec}", flush=True)
+    data = inputs.make(spec, seed=100 + i, device="cpu")
+    case = harness.GpuCase(data)
+    torch.cuda.synchronize()
+    s = spec
+    for b in range(s.batch):
+        g = s.seq_lens[b] // 4
+        off = int(data["raw_off"][b])
+        want = oracle.pool_full(data["raw_keys"][off:off + s.seq_lens[b]].numpy())
+        got = untile(case.pooled, int(case.pooled_off[b]), g, s.d_i)
+        assert np.array_equal(bits(got), bits(want)), (s.name, b)
+
+    rng = np.random.default_rng(700 + i)
+    raw = data["raw_keys"].cuda()
+    pooled = torch.full_like(case.pooled, float("nan"))
+    done = [0] * s.batch   # tokens pooled so far per sequence
+    while any(d < n for d, n in zip(done, s.seq_lens)):
+        nxt = [min(n, d + int(rng.integers(0, 9000))) for d, n in zip(done, s.seq_lens)]
+        if rng.random() < 0.3:
+            nxt = [d + 1 if d < n else d for d, n in zip(done, s.seq_lens)]  # one token
+        seq = torch.tensor(nxt, dtype=torch.int32, device="cuda")
+        first = torch.tensor([d // 4 for d in done], dtype=torch.int32, device="cuda")
+        qsa.qsa_pool_groups(case.shape, raw, case.raw_off, seq, first, pooled, case.pooled_off)
+        done = nxt
+    torch.cuda.synchronize()
+    for b in range(s.batch):
+        g = s.seq_lens[b] // 4
+        a = untile(pooled, int(case.pooled_off[b]), g, s.d_i)
+        c = untile(case.pooled, int(case.pooled_off[b]), g, s.d_i)
+        assert np.array_equal(bits(a), bits(c)), (s.name, b)
