@@ -5,7 +5,8 @@ index shapes the chunk scoring covers, causal chunk rows.  Every row must
 match the oracle (selected IDs, widths bit-exact; attention within 2e-6 of
 the exact attention over the oracle's rows), the fused and union variants
 must equal the compact one bit for bit, and the bounded dense row must equal
-the sparse one wherever the row fits the budget.
+the sparse one wherever the row fits the budget; causal-chunk rows must
+equal one decode per row bit for bit.
 
 Sources: AFN-017 "Top-k chooses the set; time chooses the order" and AFN-016
 "A sparse mask is not sparse attention".
@@ -16,6 +17,7 @@ import torch
 
 import top_sparse_attention_qsa_amd as qsa
 from tests import harness, inputs
+from tests.test_gpu_chunk import assert_same, decode_per_row
 from tests.test_gpu_parity import check_rows
 
 pytestmark = pytest.mark.gpu
@@ -77,6 +79,9 @@ def test_random_shape_matches_oracle_and_variants_agree(i):
             assert torch.equal(lse[r].view(torch.int32), ref[3][r].view(torch.int32))
         else:
             assert int(width[r]) == -1 and torch.isnan(out[r]).all(), (spec.name, r)
+    if spec.queries > 1:
+        # causal-chunk rows equal one decode per row, bit for bit
+        assert_same(case, decode_per_row(case))
     for rows in ("fused", "dedup"):
         case.decode(rows=rows)
         torch.cuda.synchronize()
