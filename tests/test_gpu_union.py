@@ -171,3 +171,21 @@ def test_dedup_out_of_range_slot_and_invalid_row():
     assert torch.all(case.width[:s.queries] == -1)
     assert torch.isnan(case.out[2 * s.queries]).all()        # token 5 is in every row of seq 2
     assert torch.isfinite(case.out[s.queries:2 * s.queries]).all()
+
+
+def test_dedup_long_rows_global_bitmaps():
+    """Rows of more than 262,144 groups: the per-row group bitmaps no longer fit
+    in LDS and are built in global memory; the result is still the compact
+    path's, and the oracle's on the longest rows."""
+    data, case = chunk_case([1_100_003, 3000], queries=4, seed=23, h_i=4, d_i=32, h_q=2,
+                            h_kv=1, d=64, budget=64)
+    assert case.shape.max_groups // 32 > 8192
+    case.decode()
+    ref = case.results()
+    case.decode(rows="dedup")
+    assert_same_results(case.results(), ref)
+    ids = ref[0].cpu().numpy()
+    for r in (0, 3):
+        exp = harness.oracle_row(data, r, exact=False)
+        w = len(exp["ids"])
+        assert np.array_equal(ids[r, :w], exp["ids"])

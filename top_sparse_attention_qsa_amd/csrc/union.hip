@@ -44,28 +44,41 @@ __device__ __forceinline__ bool width_ok(int32_t w, int32_t stride) {
   return w > 0 && w <= stride - 1;
 }
 
+// Row bitmaps of up to kMarkLdsWords words are built in LDS (LDS atomics,
+// then one coalesced write of the whole bitmap); larger ones are built in
+// place with global atomics.
+constexpr int kMarkLdsWords = 8192;  // 32 KiB: max_groups up to 262,144
+
+template <bool IN_LDS>
 __global__ void __launch_bounds__(256)
 union_mark_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__ width,
                   const int32_t* __restrict__ seq_len, int32_t queries, int32_t stride,
                   int64_t wps, int64_t row0, uint32_t* __restrict__ rbm) {
+  __shared__ uint32_t sbm[IN_LDS ? kMarkLdsWords : 1];
   const int tid = (int)threadIdx.x;
   const int64_t lrow = blockIdx.x;
   const int64_t row = row0 + lrow;
   uint32_t* bm = rbm + lrow * wps;
-  for (int64_t w = tid; w < wps; w += 256) bm[w] = 0u;
-  __threadfence();
+  uint32_t* mark = IN_LDS ? sbm : bm;
+  for (int64_t w = tid; w < wps; w += 256) mark[w] = 0u;
+  if (!IN_LDS) __threadfence();
   __syncthreads();
   const int32_t wd = width[row];
-  if (!width_ok(wd, stride)) return;
-  int32_t b;
-  const int64_t n = row_visible(seq_len, row, queries, &b);
-  const int32_t* ids = token_ids + row * stride;
-  for (int i = tid; i < wd; i += 256) {
-    const int32_t id = ids[i];
-    if (id_ok(id, n, wps)) {
-      const uint32_t g = (uint32_t)id >> 2;
-      atomicOr(&bm[g >> 5], 1u << (g & 31));
+  if (width_ok(wd, stride)) {  // an invalid row keeps an empty bitmap
+    int32_t b;
+    const int64_t n = row_visible(seq_len, row, queries, &b);
+    const int32_t* ids = token_ids + row * stride;
+    for (int i = tid; i < wd; i += 256) {
+      const int32_t id = ids[i];
+      if (id_ok(id, n, wps)) {
+        const uint32_t g = (uint32_t)id >> 2;
+        atomicOr(&mark[g >> 5], 1u << (g & 31));
+      }
     }
+  }
+  if (IN_LDS) {
+    __syncthreads();
+    for (int64_t w = tid; w < wps; w += 256) bm[w] = sbm[w];
   }
 }
 
@@ -271,8 +284,14 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   const int64_t seqs = b_last - b_first + 1;
   const int64_t words = seqs * wps;
   const int64_t nb = union_scan_blocks(words);
-  hipLaunchKernelGGL(union_mark_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a.token_ids,
-                     a.width, a.seq_len, a.queries, a.stride, wps, a.row0, a.row_bitmap);
+  if (wps <= kMarkLdsWords)
+    hipLaunchKernelGGL(union_mark_kernel<true>, dim3((unsigned)a.rows), dim3(256), 0, s,
+                       a.token_ids, a.width, a.seq_len, a.queries, a.stride, wps, a.row0,
+                       a.row_bitmap);
+  else
+    hipLaunchKernelGGL(union_mark_kernel<false>, dim3((unsigned)a.rows), dim3(256), 0, s,
+                       a.token_ids, a.width, a.seq_len, a.queries, a.stride, wps, a.row0,
+                       a.row_bitmap);
   hipLaunchKernelGGL(union_or_kernel, dim3((unsigned)((wps + 255) / 256), (unsigned)seqs),
                      dim3(256), 0, s, a.row_bitmap, a.queries, wps, a.row0, a.rows, b_first,
                      a.union_bitmap);
