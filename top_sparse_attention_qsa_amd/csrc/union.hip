@@ -16,7 +16,8 @@
 //   union_or_kernel      per sequence: OR of its rows' bitmaps
 //   union_count_kernel   popcount per block of bitmap words
 //   union_scan_kernel    exclusive scan of the block counts (one workgroup)
-//   union_list_kernel    word prefixes and the list of union groups
+//   union_list_kernel    word prefixes and the list of union groups (alone
+//                        when the bitmap fits one block)
 //   union_gather_kernel  slot-map resolution and K/V copy per union group
 //   union_pos_kernel     per row: ID -> scratch row (-1 when invalid)
 #include "qsa_internal.h"
@@ -92,8 +93,10 @@ union_or_kernel(const uint32_t* __restrict__ rbm, int32_t queries, int64_t wps, 
   const int64_t b = b_first + s;
   const int64_t r_lo = b * queries > row0 ? b * queries : row0;
   const int64_t r_end = (b + 1) * queries < row0 + rows ? (b + 1) * queries : row0 + rows;
+  // 32 rows' words in flight per round trip (the rows of a 256-query chunk
+  // take eight round trips)
   uint32_t v = 0u;
-#pragma unroll 8
+#pragma unroll 32
   for (int64_t r = r_lo; r < r_end; ++r) v |= rbm[(r - row0) * wps + w];
   ubm[s * wps + w] = v;
 }
@@ -141,15 +144,23 @@ union_scan_kernel(uint32_t* __restrict__ blk, int64_t nb, int32_t* __restrict__ 
 }
 
 // upre[w] = union groups before word w; ulist[u] = (sequence slot, group).
+// SINGLE: the bitmap fits one block, which then also writes the total to
+// blk[1] and *count_out (the count and scan kernels are not launched).
+template <bool SINGLE>
 __global__ void __launch_bounds__(kScanThreads)
 union_list_kernel(const uint32_t* __restrict__ ubm, int64_t words, int64_t wps,
-                  const uint32_t* __restrict__ blk, uint32_t cap, uint32_t* __restrict__ upre,
-                  int2* __restrict__ ulist) {
+                  uint32_t* __restrict__ blk, int32_t* __restrict__ count_out, uint32_t cap,
+                  uint32_t* __restrict__ upre, int2* __restrict__ ulist) {
   __shared__ uint32_t wave_tot[kScanThreads / kWave];
   const int64_t w0 = (int64_t)blockIdx.x * kScanWords + 4 * (int64_t)threadIdx.x;
   uint32_t v[4], c, tot;
   load_words(ubm, words, w0, v, &c);
-  uint32_t o = blk[blockIdx.x] + block_exclusive_sum<kScanThreads>(c, wave_tot, &tot);
+  uint32_t o = (SINGLE ? 0u : blk[blockIdx.x]) +
+               block_exclusive_sum<kScanThreads>(c, wave_tot, &tot);
+  if (SINGLE && threadIdx.x == 0) {
+    blk[1] = tot;
+    if (count_out) *count_out = (int32_t)tot;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t w = w0 + e;
@@ -295,17 +306,23 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(union_or_kernel, dim3((unsigned)((wps + 255) / 256), (unsigned)seqs),
                      dim3(256), 0, s, a.row_bitmap, a.queries, wps, a.row0, a.rows, b_first,
                      a.union_bitmap);
-  hipLaunchKernelGGL(union_count_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
-                     a.union_bitmap, words, a.block_prefix);
-  hipLaunchKernelGGL(union_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_prefix, nb,
-                     a.count_out);
   // capacity: a selection touches at most k+1 groups per row (k chosen, one
   // tail group); IDs from elsewhere may touch more, and groups past the
   // capacity are then neither listed nor copied, and their IDs get position -1
   const uint32_t cap = (uint32_t)(a.rows * (int64_t)(a.stride / 4));
-  hipLaunchKernelGGL(union_list_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
-                     a.union_bitmap, words, wps, a.block_prefix, cap, a.word_prefix,
-                     a.union_list);
+  if (nb == 1) {
+    hipLaunchKernelGGL(union_list_kernel<true>, dim3(1), dim3(kScanThreads), 0, s,
+                       a.union_bitmap, words, wps, a.block_prefix, a.count_out, cap,
+                       a.word_prefix, a.union_list);
+  } else {
+    hipLaunchKernelGGL(union_count_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
+                       a.union_bitmap, words, a.block_prefix);
+    hipLaunchKernelGGL(union_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_prefix, nb,
+                       a.count_out);
+    hipLaunchKernelGGL(union_list_kernel<false>, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
+                       a.union_bitmap, words, wps, a.block_prefix, nullptr, cap, a.word_prefix,
+                       a.union_list);
+  }
   const int32_t row_f4 = a.kv_heads * a.head_dim / 4;
   const int64_t pairs = ((int64_t)cap + 1) / 2;
   const int64_t max_grid = (int64_t)a.cus * 8;
