@@ -457,6 +457,33 @@ def main():
     fused_stage_ms, _ = stage_loop(True)
     assert torch.equal(case.out, ref_out), "fused path differs from the compact path"
 
+    # the compact step captured once in a HIP graph and replayed K times (a
+    # decode call enqueues kernel launches only, so it can be captured)
+    print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        case.decode()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        case.decode()
+    case.out.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(case.out, ref_out), "graph replay differs from the eager step"
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop) / args.steps
+    assert torch.equal(case.out, ref_out), "graph replay differs from the eager step"
+    del graph
+
     alg = algorithmic_bytes()
     step_bytes = sum(alg.values())
     achieved = alg["score"] / (score_ms * 1e-3) / 1e9
@@ -518,6 +545,12 @@ def main():
             "mean_launch_ms": score_ms,
             "timing": "HIP events on the launch stream around the kernel, averaged over the "
                       "per-stage loop's steps",
+        },
+        "graph": {
+            "note": "the compact step captured in a HIP graph, K replays; bit-identical "
+                    "outputs (context: value is the eager K steps)",
+            "value": rows / (graph_ms * 1e-3),
+            "ms_per_step": graph_ms,
         },
         "fused": {
             "note": "same step with resolve+gather fused into the attention kernel "
