@@ -68,11 +68,11 @@ def source_digest():
 
 
 def library_digest():
-    """Digest of every HIP source of the library (the step's kernels)."""
+    """Digest of every source of the library (kernels and host side)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "top_sparse_attention_qsa_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith((".hip", ".h", ".cpp")):
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode())
                 h.update(fh.read())
@@ -106,29 +106,47 @@ def measured_step_traffic():
     return c.get("stage_traffic_bytes")
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_stream_read.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_stream_read.so")
+
+
+def build_probe():
+    """Compile the streaming-read probe of the context line (not part of
+    libqsa) next to this file."""
+    import subprocess
+    from top_sparse_attention_qsa_amd import build as qsa_build
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [qsa_build.hipcc(), *qsa_build.HIPFLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def context_bandwidth(reps=10):
     """Achievable-bandwidth context, not a denominator of anything reported:
-    a plain streaming read of 1 GiB (bwprobe/stream_read.hip, grid-stride
+    a plain streaming read of 1 GiB (bench_stream_read.hip, grid-stride
     float4 loads) and torch's device copy of 1 GiB."""
     import ctypes
     import torch
-    from top_sparse_attention_qsa_amd import build as qsa_build
     n = (1 << 30) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     res = {}
     fns = [("copy", lambda: y.copy_(x), 8 * n)]
-    if os.path.exists(qsa_build.BW_LIB):
-        bw = ctypes.CDLL(qsa_build.BW_LIB)
-        bw.bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                      ctypes.c_void_p]
+    if not os.path.exists(PROBE_LIB):
+        build_probe()
+    bw = ctypes.CDLL(PROBE_LIB)
+    bw.bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
 
-        def read():
-            s = torch.cuda.current_stream().cuda_stream
-            if bw.bw_stream_read(x.data_ptr(), 4 * n, sink.data_ptr(), s) != 0:
-                raise RuntimeError("bw_stream_read failed")
-        fns.insert(0, ("stream_read", read, 4 * n))
+    def read():
+        s = torch.cuda.current_stream().cuda_stream
+        if bw.bw_stream_read(x.data_ptr(), 4 * n, sink.data_ptr(), s) != 0:
+            raise RuntimeError("bw_stream_read failed")
+    fns.insert(0, ("stream_read", read, 4 * n))
     for name, fn, nbytes in fns:
         for _ in range(3):
             fn()

@@ -1,7 +1,7 @@
-// stream_read.hip -- a plain streaming read of a device buffer, for the
-// "achievable bandwidth" context line of the benchmark.  Not part of libqsa:
-// it computes nothing of the attention path and is built into its own
-// library, libbwprobe.so.
+// bench_stream_read.hip -- a plain streaming read of a device buffer, for the
+// "achievable bandwidth" context line of bench.py.  Not part of libqsa: it
+// computes nothing of the attention path and is built into its own small
+// library next to bench.py (bench_stream_read.so).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 

@@ -138,9 +138,9 @@ typedef struct qsa_bytes {
 
 /* Workspace bytes qsa_decode needs for this shape (also enough for
  * qsa_select_topk and qsa_online_attend).  Grows with rows_in_flight x
- * (max_groups + 4k+4), never with rows x tokens ([MASK] §What the
- * checkpoint measures: groups plus budget plus selected width).  0 on an
- * invalid shape. */
+ * (max_groups + 4k+4): per row in flight, one score per candidate group and
+ * the selected width's K/V rows, and no buffer spanning rows x tokens
+ * ([MASK] §What the checkpoint measures).  0 on an invalid shape. */
 QSA_API size_t qsa_workspace_bytes(const qsa_shape *shape);
 
 /* Pool complete groups into the tiled pooled-key buffer: for every
@@ -251,11 +251,12 @@ QSA_API int qsa_decode(const qsa_shape *shape, const float *index_q, const float
 
 /* Steps 1-8 with steps 6-8 fused: the attention kernel resolves each
  * selected logical ID once through the slot map and reads the K/V rows
- * straight from the cache, so no compact scratch is written or read
- * ([MASK] §Why compact gather comes before fusion: a later fused
- * indirect-load kernel may replace the gather, keeping the logical-ID
- * contract and the zero dense-mask allocation).  Same arguments, workspace
- * and results as qsa_decode, bit for bit; the timer's gather stage is empty. */
+ * straight from the cache, so no compact scratch is written or read.  The
+ * note names this as the step after the compact gather, once measured, with
+ * the logical-ID interface and the absence of any dense mask unchanged
+ * ([MASK] §Why compact gather comes before fusion).  Same arguments,
+ * workspace and results as qsa_decode, bit for bit; the timer's gather stage
+ * is empty. */
 QSA_API int qsa_decode_fused(const qsa_shape *shape, const float *index_q, const float *pooled,
                              const int64_t *pooled_off, const int32_t *seq_len,
                              const int32_t *slot_map, const int64_t *slot_off,

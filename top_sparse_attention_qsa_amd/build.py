@@ -1,5 +1,9 @@
-"""Compile the HIP sources in csrc/ into top_sparse_attention_qsa_amd/libqsa.so
-for gfx950 with hipcc (cross-compiles without a GPU)."""
+"""Compile libqsa.so for gfx950 (cross-compiles without a GPU).
+
+The HIP sources in csrc/ (*.hip: kernels and their launchers) go through
+hipcc; the host side (*.cpp: validation, workspace layout, launch chains,
+accounting) is plain C++ and goes through the host compiler alone, which is
+what keeps it free of HIP types and buildable under the sanitizers."""
 import os
 import shutil
 import subprocess
@@ -11,9 +15,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
-# a streaming-read kernel for the benchmark's bandwidth context line (not libqsa)
-BW_SRC = os.path.join(PKG, "bwprobe", "stream_read.hip")
-BW_LIB = os.path.join(PKG, "bwprobe", "libbwprobe.so")
 BUILD = os.path.join(ROOT, "_build", "qsa")
 
 ARCH = "gfx950"
@@ -29,6 +30,8 @@ HIPFLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",
+            "-I", INCLUDE, "-I", CSRC]
 
 
 def hipcc():
@@ -38,22 +41,29 @@ def hipcc():
     return exe
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def cxx():
+    return shutil.which("g++") or "c++"
+
+
+def sources(ext):
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(ext))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".hip"):
+        cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [cxx(), *CXXFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+    srcs = sources(".hip") + sources(".cpp")
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
@@ -62,14 +72,8 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    tmp = BW_LIB + ".tmp"
-    cmd = [hipcc(), *HIPFLAGS, "-shared", "-o", tmp, BW_SRC]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {BW_SRC}:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, BW_LIB)
     if verbose:
-        print(f"built {LIB} and {BW_LIB}")
+        print(f"built {LIB}")
     return LIB
 
 

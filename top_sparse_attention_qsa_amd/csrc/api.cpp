@@ -1,13 +1,18 @@
-// api.hip -- host side of libqsa.so: validation, workspace layout, launch
-// chain, stage timer and byte accounting.  Every entry point validates its
+// api.cpp -- host side of libqsa.so: validation, workspace layout, launch
+// chains, stage timer and byte accounting.  Every entry point validates its
 // arguments on the host and returns a qsa_status before enqueueing anything.
 // No C++ exception crosses the ABI; no device memory is allocated.
+//
+// Plain C++: the kernels are reached only through the launchers of
+// qsa_launch.h, so this file builds with a host compiler alone (and, for the
+// sanitizer tests, against a stub that records the launches).
 #include <stdint.h>
 #include <string.h>
 
 #include <new>
 
-#include "qsa_internal.h"
+#include "qsa.h"
+#include "qsa_launch.h"
 
 using namespace qsa;
 
@@ -100,14 +105,14 @@ Layout layout(const qsa_shape* s) {
   L.ublk = off;
   off = align256(off + (size_t)(union_scan_blocks(useq * wps) + 1) * sizeof(uint32_t));
   L.ulist = off;
-  off = align256(off + (size_t)R * (s->budget_groups + 1) * sizeof(int2));
+  off = align256(off + (size_t)R * (s->budget_groups + 1) * 2 * sizeof(int32_t));
   L.upos = off;
   off = align256(off + (size_t)R * token_stride(s) * sizeof(int32_t));
   L.total = off;
   return L;
 }
 
-inline int hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+inline int hip_status(int e) { return e == 0 ? QSA_OK : QSA_ERR_HIP; }
 
 }  // namespace
 
@@ -115,12 +120,12 @@ struct qsa_timer {
   int32_t max_calls;
   int32_t calls;
   uint32_t mask;   // stages timed (bit s: stage s)
-  hipEvent_t* ev;  // [max_calls][QSA_DECODE_STAGES + 1]
+  void** ev;       // hipEvent_t [max_calls][QSA_DECODE_STAGES + 1]
 };
 
 extern "C" {
 
-const char* qsa_version(void) { return "qsa 0.1.0 gfx950"; }
+const char* qsa_version(void) { return "qsa 0.2.0 gfx950"; }
 
 const char* qsa_status_string(int status) {
   switch (status) {
@@ -166,7 +171,7 @@ int qsa_pool_groups(const qsa_shape* s, const float* raw_keys, const int64_t* ra
   if (!aligned16(raw_keys) || !aligned16(pooled)) return QSA_ERR_SHAPE;
   PoolArgs a{raw_keys, raw_off, seq_len, first_group, pooled, pooled_off, s->batch,
              s->index_dim, s->max_groups};
-  return hip_status(launch_pool(a, (hipStream_t)stream));
+  return hip_status(launch_pool(a, stream));
 }
 
 int qsa_score_groups(const qsa_shape* s, const float* index_q, const float* pooled,
@@ -178,7 +183,7 @@ int qsa_score_groups(const qsa_shape* s, const float* index_q, const float* pool
   if (!aligned16(pooled) || !aligned16(scores)) return QSA_ERR_SHAPE;
   ScoreArgs a{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups,
               0, row_count(s), scores, nullptr};
-  return hip_status(launch_score(a, s->index_heads, s->index_dim, (hipStream_t)stream));
+  return hip_status(launch_score(a, s->index_heads, s->index_dim, stream));
 }
 
 int qsa_score_groups_chunk(const qsa_shape* s, const float* index_q, const float* pooled,
@@ -191,7 +196,7 @@ int qsa_score_groups_chunk(const qsa_shape* s, const float* index_q, const float
   if (!chunk_supported(s->index_heads, s->queries, row_count(s))) return QSA_ERR_UNSUPPORTED;
   ChunkArgs a{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, 0, row_count(s),
               approx, bound, nullptr, nullptr};
-  return hip_status(launch_chunk(a, s->index_heads, s->index_dim, (hipStream_t)stream));
+  return hip_status(launch_chunk(a, s->index_heads, s->index_dim, stream));
 }
 
 int qsa_select_topk(const qsa_shape* s, const float* scores, const int32_t* seq_len,
@@ -204,16 +209,16 @@ int qsa_select_topk(const qsa_shape* s, const float* scores, const int32_t* seq_
   if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
   uint32_t* maxima = reinterpret_cast<uint32_t*>((char*)ws + L.maxima);
   const int64_t rows = row_count(s), R = rows_per_pass(s);
-  hipStream_t st = (hipStream_t)stream;
+  void* st = stream;
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
     const int64_t n = (rows - r0) < R ? (rows - r0) : R;
     const float* sc = scores + r0 * s->max_groups;
-    hipError_t e = launch_segment_maxima(sc, seq_len, s->queries, s->max_groups, r0, n, maxima, st);
-    if (e != hipSuccess) return QSA_ERR_HIP;
+    int e = launch_segment_maxima(sc, seq_len, s->queries, s->max_groups, r0, n, maxima, st);
+    if (e != 0) return QSA_ERR_HIP;
     SelectArgs a{sc, maxima, seq_len, s->queries, s->max_groups, s->budget_groups,
                  r0, n, sel_bitmap, nullptr, nullptr};
     e = launch_select(a, st);
-    if (e != hipSuccess) return QSA_ERR_HIP;
+    if (e != 0) return QSA_ERR_HIP;
   }
   return QSA_OK;
 }
@@ -226,7 +231,7 @@ int qsa_emit_chronological(const qsa_shape* s, const uint32_t* sel_bitmap, const
   if (!aligned16(token_ids)) return QSA_ERR_SHAPE;
   return hip_status(launch_emit(sel_bitmap, seq_len, s->queries, s->max_groups,
                                 s->budget_groups, row_count(s), token_ids, width,
-                                (hipStream_t)stream));
+                                stream));
 }
 
 int qsa_resolve_gather(const qsa_shape* s, const int32_t* token_ids, const int32_t* width,
@@ -244,7 +249,7 @@ int qsa_resolve_gather(const qsa_shape* s, const int32_t* token_ids, const int32
   GatherArgs a{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
                s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, 0, row_count(s),
                k_compact, v_compact, phys_slots};
-  return hip_status(launch_gather(a, (hipStream_t)stream));
+  return hip_status(launch_gather(a, stream));
 }
 
 int qsa_online_attend(const qsa_shape* s, const float* q, const float* k_compact,
@@ -259,7 +264,7 @@ int qsa_online_attend(const qsa_shape* s, const float* q, const float* k_compact
   if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
   const int64_t rows = row_count(s), R = rows_per_pass(s);
   const int64_t compact_row = (int64_t)token_stride(s) * s->kv_heads * s->head_dim;
-  hipStream_t st = (hipStream_t)stream;
+  void* st = stream;
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
     const int64_t n = (rows - r0) < R ? (rows - r0) : R;
     AttendArgs a{q, k_compact + r0 * compact_row, v_compact + r0 * compact_row, width,
@@ -267,8 +272,8 @@ int qsa_online_attend(const qsa_shape* s, const float* q, const float* k_compact
                  softmax_scale, r0, n,
                  reinterpret_cast<float*>((char*)ws + L.pacc),
                  reinterpret_cast<float*>((char*)ws + L.pml), out, lse};
-    if (launch_attend(a, st) != hipSuccess) return QSA_ERR_HIP;
-    if (launch_merge(a, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_attend(a, st) != 0) return QSA_ERR_HIP;
+    if (launch_merge(a, st) != 0) return QSA_ERR_HIP;
   }
   return QSA_OK;
 }
@@ -280,7 +285,7 @@ int qsa_timer_create(int32_t max_calls, uint32_t stage_mask, qsa_timer** timer) 
   qsa_timer* t = new (std::nothrow) qsa_timer;
   if (!t) return QSA_ERR_HIP;
   const int32_t n = max_calls * (QSA_DECODE_STAGES + 1);
-  t->ev = new (std::nothrow) hipEvent_t[n];
+  t->ev = new (std::nothrow) void*[n];
   t->max_calls = max_calls;
   t->calls = 0;
   t->mask = stage_mask;
@@ -289,8 +294,8 @@ int qsa_timer_create(int32_t max_calls, uint32_t stage_mask, qsa_timer** timer) 
     return QSA_ERR_HIP;
   }
   for (int32_t i = 0; i < n; ++i) {
-    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
-      for (int32_t j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
+    if (event_create(&t->ev[i]) != 0) {
+      for (int32_t j = 0; j < i; ++j) (void)event_destroy(t->ev[j]);
       delete[] t->ev;
       delete t;
       return QSA_ERR_HIP;
@@ -303,14 +308,14 @@ int qsa_timer_create(int32_t max_calls, uint32_t stage_mask, qsa_timer** timer) 
 int qsa_timer_read(qsa_timer* t, float* ms, int32_t* calls) {
   if (!t || !ms || !calls) return QSA_ERR_NULL;
   for (int32_t c = 0; c < t->calls; ++c) {
-    hipEvent_t* e = t->ev + (size_t)c * (QSA_DECODE_STAGES + 1);
+    void** e = t->ev + (size_t)c * (QSA_DECODE_STAGES + 1);
     int last = QSA_DECODE_STAGES;  // the last event recorded for this call
     while (last > 0 && !((t->mask >> (last - 1)) & 1u)) --last;
-    if (hipEventSynchronize(e[last]) != hipSuccess) return QSA_ERR_HIP;
+    if (event_synchronize(e[last]) != 0) return QSA_ERR_HIP;
     for (int st = 0; st < QSA_DECODE_STAGES; ++st) {
       float v = -1.0f;  // stage not timed
       if ((t->mask >> st) & 1u) {
-        if (hipEventElapsedTime(&v, e[st], e[st + 1]) != hipSuccess) return QSA_ERR_HIP;
+        if (event_elapsed_ms(&v, e[st], e[st + 1]) != 0) return QSA_ERR_HIP;
       }
       ms[(size_t)c * QSA_DECODE_STAGES + st] = v;
     }
@@ -326,7 +331,7 @@ void qsa_timer_reset(qsa_timer* t) {
 void qsa_timer_destroy(qsa_timer* t) {
   if (!t) return;
   const int32_t n = t->max_calls * (QSA_DECODE_STAGES + 1);
-  for (int32_t i = 0; i < n; ++i) (void)hipEventDestroy(t->ev[i]);
+  for (int32_t i = 0; i < n; ++i) (void)event_destroy(t->ev[i]);
   delete[] t->ev;
   delete t;
 }
@@ -362,7 +367,7 @@ static UnionArgs union_args(const qsa_shape* s, const Layout& L, char* w, const 
   u.union_bitmap = reinterpret_cast<uint32_t*>(w + L.ubm);
   u.word_prefix = reinterpret_cast<uint32_t*>(w + L.upre);
   u.block_prefix = reinterpret_cast<uint32_t*>(w + L.ublk);
-  u.union_list = reinterpret_cast<int2*>(w + L.ulist);
+  u.union_list = reinterpret_cast<int32_t*>(w + L.ulist);
   u.k_union = k_union;
   u.v_union = v_union;
   u.union_pos = union_pos;
@@ -395,8 +400,8 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
   float* vc = reinterpret_cast<float*>(w + L.vc);
   float* pacc = reinterpret_cast<float*>(w + L.pacc);
   float* pml = reinterpret_cast<float*>(w + L.pml);
-  hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = timer ? timer->ev + (size_t)timer->calls * (QSA_DECODE_STAGES + 1) : nullptr;
+  void* st = stream;
+  void** ev = timer ? timer->ev + (size_t)timer->calls * (QSA_DECODE_STAGES + 1) : nullptr;
   const int64_t rows = row_count(s), R = rows_per_pass(s);
   // causal chunks score on MFMA with certified bounds and an exact rescoring
   // of the candidates; decode rows (or unsupported chunk shapes) use the chain
@@ -411,25 +416,25 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
       if (!timed) return true;
       const uint32_t m = timer->mask;
       const bool need = ((m >> i) & 1u) || (i > 0 && ((m >> (i - 1)) & 1u));
-      return !need || hipEventRecord(ev[i], st) == hipSuccess;
+      return !need || event_record(ev[i], st) == 0;
     };
     if (!record(0)) return QSA_ERR_HIP;
     if (chunk) {
       ChunkArgs ca{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
                    nullptr, nullptr, scores, maxima};
-      if (launch_chunk(ca, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
+      if (launch_chunk(ca, s->index_heads, s->index_dim, st) != 0) return QSA_ERR_HIP;
     } else {
       ScoreArgs sa{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
                    scores, maxima};
-      if (launch_score(sa, s->index_heads, s->index_dim, st) != hipSuccess) return QSA_ERR_HIP;
+      if (launch_score(sa, s->index_heads, s->index_dim, st) != 0) return QSA_ERR_HIP;
     }
     if (!record(1)) return QSA_ERR_HIP;
     SelectArgs se{scores, maxima, seq_len, s->queries, s->max_groups, s->budget_groups,
                   r0, n, nullptr, token_ids, width};
     if (chunk) {
       RescoreArgs ra{index_q, pooled, pooled_off, s->index_heads, s->index_dim};
-      if (launch_select_certified(se, ra, st) != hipSuccess) return QSA_ERR_HIP;
-    } else if (launch_select(se, st) != hipSuccess) {
+      if (launch_select_certified(se, ra, st) != 0) return QSA_ERR_HIP;
+    } else if (launch_select(se, st) != 0) {
       return QSA_ERR_HIP;
     }
     if (!record(2)) return QSA_ERR_HIP;
@@ -438,11 +443,11 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
       GatherArgs ga{token_ids, width, seq_len, slot_map, slot_off, k_cache, v_cache, s->queries,
                     s->kv_heads, s->head_dim, token_stride(s), s->kv_slots, r0, n, kc, vc,
                     nullptr};
-      if (launch_gather(ga, st) != hipSuccess) return QSA_ERR_HIP;
+      if (launch_gather(ga, st) != 0) return QSA_ERR_HIP;
     } else if (mode == Rows::kUnion) {
       const UnionArgs ua = union_args(s, L, w, token_ids, width, seq_len, slot_map, slot_off,
                                       k_cache, v_cache, r0, n, kc, vc, upos, nullptr);
-      if (launch_union(ua, st) != hipSuccess) return QSA_ERR_HIP;
+      if (launch_union(ua, st) != 0) return QSA_ERR_HIP;
     }
     if (!record(3)) return QSA_ERR_HIP;
     AttendArgs aa{q, kc, vc, width, s->q_heads, s->kv_heads, s->head_dim, token_stride(s),
@@ -462,9 +467,9 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
       aa.kv_slots = s->kv_slots;
       aa.queries = s->queries;
     }
-    if (launch_attend(aa, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_attend(aa, st) != 0) return QSA_ERR_HIP;
     if (!record(4)) return QSA_ERR_HIP;
-    if (launch_merge(aa, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_merge(aa, st) != 0) return QSA_ERR_HIP;
     if (!record(5)) return QSA_ERR_HIP;
   }
   if (timer) timer->calls += 1;
@@ -488,10 +493,9 @@ int qsa_dense_attend(const qsa_shape* s, const int32_t* seq_len, const int32_t* 
     return QSA_ERR_SHAPE;
   const Layout L = layout(s);
   if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  void* st = stream;
   const int64_t rows = row_count(s), R = rows_per_pass(s);
-  if (launch_dense_ids(seq_len, s->queries, s->budget_groups, rows, token_ids, width, st) !=
-      hipSuccess)
+  if (launch_dense_ids(seq_len, s->queries, s->budget_groups, rows, token_ids, width, st) != 0)
     return QSA_ERR_HIP;
   char* w = (char*)ws;
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
@@ -508,8 +512,8 @@ int qsa_dense_attend(const qsa_shape* s, const int32_t* seq_len, const int32_t* 
     aa.v_cache = v_cache;
     aa.kv_slots = s->kv_slots;
     aa.queries = s->queries;
-    if (launch_attend(aa, st) != hipSuccess) return QSA_ERR_HIP;
-    if (launch_merge(aa, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_attend(aa, st) != 0) return QSA_ERR_HIP;
+    if (launch_merge(aa, st) != 0) return QSA_ERR_HIP;
   }
   return QSA_OK;
 }
@@ -565,7 +569,7 @@ int qsa_union_gather(const qsa_shape* s, const int32_t* token_ids, const int32_t
   const UnionArgs ua = union_args(s, L, (char*)ws, token_ids, width, seq_len, slot_map, slot_off,
                                   k_cache, v_cache, 0, row_count(s), k_union, v_union, union_pos,
                                   union_groups);
-  return hip_status(launch_union(ua, (hipStream_t)stream));
+  return hip_status(launch_union(ua, stream));
 }
 
 int qsa_online_attend_indexed(const qsa_shape* s, const float* q, const float* k_rows,
@@ -581,7 +585,7 @@ int qsa_online_attend_indexed(const qsa_shape* s, const float* q, const float* k
   const Layout L = layout(s);
   if (ws_bytes < L.total) return QSA_ERR_WORKSPACE;
   const int64_t rows = row_count(s), R = rows_per_pass(s);
-  hipStream_t st = (hipStream_t)stream;
+  void* st = stream;
   for (int64_t r0 = 0; r0 < rows; r0 += R) {
     const int64_t n = (rows - r0) < R ? (rows - r0) : R;
     AttendArgs a{q, nullptr, nullptr, width, s->q_heads, s->kv_heads, s->head_dim,
@@ -592,8 +596,8 @@ int qsa_online_attend_indexed(const qsa_shape* s, const float* q, const float* k
     a.k_cache = k_rows;
     a.v_cache = v_rows;
     a.kv_slots = n_rows;
-    if (launch_attend(a, st) != hipSuccess) return QSA_ERR_HIP;
-    if (launch_merge(a, st) != hipSuccess) return QSA_ERR_HIP;
+    if (launch_attend(a, st) != 0) return QSA_ERR_HIP;
+    if (launch_merge(a, st) != 0) return QSA_ERR_HIP;
   }
   return QSA_OK;
 }

@@ -615,14 +615,6 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
 
 }  // namespace
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return cus > 0 ? cus : 256;
-}
-
 namespace {
 
 // Persistent launch: as many workgroups as can be resident at once (queried
@@ -677,8 +669,9 @@ hipError_t launch_attend_d(const AttendArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+int launch_attend(const AttendArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.head_dim) {
     case 64: return launch_attend_d<64>(a, s);
     case 128: return launch_attend_d<128>(a, s);
@@ -686,8 +679,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   }
 }
 
-hipError_t launch_merge(const AttendArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+int launch_merge(const AttendArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid((unsigned)a.q_heads, (unsigned)a.rows);
   switch (a.head_dim) {
     case 64:

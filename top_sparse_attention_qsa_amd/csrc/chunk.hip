@@ -242,13 +242,8 @@ hipError_t launch_chunk_h(const ChunkArgs& a, int d_i, hipStream_t s) {
 
 }  // namespace
 
-bool chunk_supported(int h_i, int queries, int64_t rows_per_launch) {
-  if (h_i != 4 && h_i != 8 && h_i != 16) return false;
-  const int rb = 4 * (16 / h_i);
-  return queries % rb == 0 && rows_per_launch % rb == 0;
-}
-
-hipError_t launch_chunk(const ChunkArgs& a, int h_i, int d_i, hipStream_t s) {
+int launch_chunk(const ChunkArgs& a, int h_i, int d_i, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (h_i) {
     case 4: return launch_chunk_h<4>(a, d_i, s);
     case 8: return launch_chunk_h<8>(a, d_i, s);

@@ -109,8 +109,9 @@ gather_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+int launch_gather(const GatherArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t row_f4 = a.kv_heads * a.head_dim / 4;
   dim3 grid((unsigned)((a.stride + kGatherTokens - 1) / kGatherTokens), (unsigned)a.rows);
   hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, a.token_ids, a.width, a.seq_len,

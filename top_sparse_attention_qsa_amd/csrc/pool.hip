@@ -65,7 +65,8 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
+int launch_pool(const PoolArgs& a, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.index_dim) {
     case 32: return launch_pool_t<32>(a, s);
     case 64: return launch_pool_t<64>(a, s);

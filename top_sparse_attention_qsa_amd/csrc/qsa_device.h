@@ -5,15 +5,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsa_launch.h"
+
 namespace qsa {
 
 constexpr int kWave = 64;
 constexpr int kScoreWaves = 4;        // waves (one 64-group tile each) per scoring workgroup
-constexpr int kSegment = 16;          // groups per maximum used to bound the threshold
 constexpr int kSelectThreads = 1024;  // one selection workgroup per row
 constexpr int kCandCap = 4096;        // candidates kept in LDS before the streaming path
 constexpr int kGatherTokens = 8;      // compact rows per gather workgroup
-constexpr int kAttnChunk = 64;        // compact rows per attention partial
 
 // Scores are ordered through a monotone unsigned key: -0 is folded onto +0,
 // then non-negative floats get their sign bit set and negative floats are

@@ -141,7 +141,8 @@ hipError_t launch_score_h(const ScoreArgs& a, int d_i, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_score(const ScoreArgs& a, int h_i, int d_i, hipStream_t s) {
+int launch_score(const ScoreArgs& a, int h_i, int d_i, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (h_i) {
     case 1: return launch_score_h<1>(a, d_i, s);
     case 2: return launch_score_h<2>(a, d_i, s);
@@ -152,14 +153,15 @@ hipError_t launch_score(const ScoreArgs& a, int h_i, int d_i, hipStream_t s) {
   }
 }
 
-hipError_t launch_segment_maxima(const float* scores, const int32_t* seq_len, int32_t queries,
-                                 int64_t g_max, int64_t row0, int64_t rows, uint32_t* maxima,
-                                 hipStream_t s) {
+int launch_segment_maxima(const float* scores, const int32_t* seq_len, int32_t queries,
+                          int64_t g_max, int64_t row0, int64_t rows, uint32_t* maxima,
+                          void* stream) {
   const int64_t segs = g_max / kSegment;
   dim3 grid((unsigned)((segs + 255) / 256), (unsigned)rows);
-  if (grid.x == 0 || rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(segment_maxima_kernel, grid, dim3(256), 0, s, scores, seq_len, queries,
-                     g_max, row0, maxima);
+  if (grid.x == 0 || rows == 0) return 0;
+  hipLaunchKernelGGL(segment_maxima_kernel, grid, dim3(256), 0,
+                     static_cast<hipStream_t>(stream), scores, seq_len, queries, g_max, row0,
+                     maxima);
   return hipGetLastError();
 }
 

@@ -665,17 +665,18 @@ dense_ids_kernel(const int32_t* __restrict__ seq_len, int32_t queries, int32_t k
 
 }  // namespace
 
-hipError_t launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, int64_t rows,
-                            int32_t* token_ids, int32_t* width, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(dense_ids_kernel, dim3((unsigned)rows), dim3(256), 0, s, seq_len, queries, k,
-                     token_ids, width);
+int launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, int64_t rows,
+                     int32_t* token_ids, int32_t* width, void* stream) {
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(dense_ids_kernel, dim3((unsigned)rows), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), seq_len, queries, k, token_ids, width);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.rows), dim3(NT), 0, s, a.scores, a.maxima,
+int launch_select(const SelectArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.rows), dim3(NT), 0,
+                     static_cast<hipStream_t>(stream), a.scores, a.maxima,
                      a.seq_len, a.queries, a.g_max, a.k, a.row0, a.bitmap, a.token_ids,
                      a.width);
   return hipGetLastError();
@@ -699,8 +700,9 @@ hipError_t launch_cert_h(const SelectArgs& a, const RescoreArgs& r, hipStream_t 
   }
 }
 
-hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+int launch_select_certified(const SelectArgs& a, const RescoreArgs& r, void* stream) {
+  if (a.rows == 0) return 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (r.index_heads) {
     case 4: return launch_cert_h<4>(a, r, s);
     case 8: return launch_cert_h<8>(a, r, s);
@@ -709,12 +711,12 @@ hipError_t launch_select_certified(const SelectArgs& a, const RescoreArgs& r, hi
   }
 }
 
-hipError_t launch_emit(const uint32_t* bitmap, const int32_t* seq_len, int32_t queries,
-                       int64_t g_max, int32_t k, int64_t rows, int32_t* token_ids,
-                       int32_t* width, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)rows), dim3(NT), 0, s, bitmap, seq_len, queries,
-                     g_max, k, token_ids, width);
+int launch_emit(const uint32_t* bitmap, const int32_t* seq_len, int32_t queries, int64_t g_max,
+                int32_t k, int64_t rows, int32_t* token_ids, int32_t* width, void* stream) {
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)rows), dim3(NT), 0,
+                     static_cast<hipStream_t>(stream), bitmap, seq_len, queries, g_max, k,
+                     token_ids, width);
   return hipGetLastError();
 }
 

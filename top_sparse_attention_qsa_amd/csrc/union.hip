@@ -26,7 +26,8 @@ namespace qsa {
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanWords = 4 * kScanThreads;  // bitmap words per count/list block
+constexpr int kScanWords = kUnionScanWords;  // bitmap words per count/list block
+static_assert(kScanWords == 4 * kScanThreads, "four words per scan thread");
 
 // Visible tokens of a row (negative: no such row in its sequence).
 __device__ __forceinline__ int64_t row_visible(const int32_t* seq_len, int64_t row,
@@ -278,17 +279,10 @@ union_pos_kernel(const int32_t* __restrict__ token_ids, const int32_t* __restric
 
 }  // namespace
 
-int64_t union_words_per_seq(int64_t max_groups) { return max_groups / 32 + 1; }
-
-int64_t union_seqs_per_pass(int64_t rows_per_pass, int32_t queries, int32_t batch) {
-  const int64_t s = rows_per_pass / queries + 2;
-  return s < batch ? s : batch;
-}
-
-int64_t union_scan_blocks(int64_t words) { return (words + kScanWords - 1) / kScanWords; }
-
-hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
+int launch_union(const UnionArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int2* union_list = reinterpret_cast<int2*>(a.union_list);
   const int64_t wps = union_words_per_seq(a.max_groups);
   const int64_t b_first = a.row0 / a.queries;
   const int64_t b_last = (a.row0 + a.rows - 1) / a.queries;
@@ -313,7 +307,7 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   if (nb == 1) {
     hipLaunchKernelGGL(union_list_kernel<true>, dim3(1), dim3(kScanThreads), 0, s,
                        a.union_bitmap, words, wps, a.block_prefix, a.count_out, cap,
-                       a.word_prefix, a.union_list);
+                       a.word_prefix, union_list);
   } else {
     hipLaunchKernelGGL(union_count_kernel, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
                        a.union_bitmap, words, a.block_prefix);
@@ -321,14 +315,14 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
                        a.count_out);
     hipLaunchKernelGGL(union_list_kernel<false>, dim3((unsigned)nb), dim3(kScanThreads), 0, s,
                        a.union_bitmap, words, wps, a.block_prefix, nullptr, cap, a.word_prefix,
-                       a.union_list);
+                       union_list);
   }
   const int32_t row_f4 = a.kv_heads * a.head_dim / 4;
   const int64_t pairs = ((int64_t)cap + 1) / 2;
   const int64_t max_grid = (int64_t)a.cus * 8;
   hipLaunchKernelGGL(union_gather_kernel, dim3((unsigned)(pairs < max_grid ? pairs : max_grid)),
                      dim3(256),
-                     0, s, a.union_list, a.block_prefix + nb, a.seq_len, a.slot_map, a.slot_off,
+                     0, s, union_list, a.block_prefix + nb, a.seq_len, a.slot_map, a.slot_off,
                      reinterpret_cast<const float4*>(a.k_cache),
                      reinterpret_cast<const float4*>(a.v_cache), a.queries, row_f4, a.kv_slots,
                      a.row0, a.rows, b_first, cap, reinterpret_cast<float4*>(a.k_union),
