@@ -70,7 +70,9 @@ typedef enum {
     QSA_ERR_BUDGET = 3,      /* budget_groups outside [1, QSA_MAX_BUDGET]       */
     QSA_ERR_WORKSPACE = 4,   /* workspace smaller than qsa_workspace_bytes()    */
     QSA_ERR_HIP = 5,         /* a HIP call or kernel launch failed              */
-    QSA_ERR_UNSUPPORTED = 6  /* a valid shape this build has no kernel for      */
+    QSA_ERR_UNSUPPORTED = 6, /* a valid shape this build has no kernel for      */
+    QSA_ERR_STATIC_WORKSPACE = 7 /* qsa_decode_noalloc: the shape needs more than
+                                    QSA_NOALLOC_WORKSPACE_BYTES of workspace      */
 } qsa_status;
 
 /* Problem shape.  Supported: index_dim in {32, 64, 128}; index_heads in
@@ -332,6 +334,27 @@ QSA_API int qsa_decode_dedup(const qsa_shape *shape, const float *index_q, const
                              float softmax_scale, int32_t *token_ids, int32_t *width, float *out,
                              float *lse, void *workspace, size_t workspace_bytes,
                              qsa_timer *timer, qsa_stream stream);
+
+/* qsa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * workspace is the library's own static device buffer of
+ * QSA_NOALLOC_WORKSPACE_BYTES (64 MiB), which each device the library runs on
+ * holds until the process ends; the call allocates nothing.  Same arguments
+ * as qsa_decode minus the workspace, same results bit for bit.  A shape
+ * whose qsa_workspace_bytes exceeds the buffer returns
+ * QSA_ERR_STATIC_WORKSPACE before anything is enqueued: lower rows_in_flight
+ * (at 262,144 visible tokens, indexer 16 x 128 and attention 32 / 4 x 128,
+ * budget 512, up to 7 rows fit).  Nothing in the buffer has to start at zero
+ * (every call writes what it reads); calls that overlap on one device share
+ * the buffer and race, so calls on one device must be ordered (one stream, or
+ * streams joined by events). */
+#define QSA_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+QSA_API int qsa_decode_noalloc(const qsa_shape *shape, const float *index_q, const float *pooled,
+                               const int64_t *pooled_off, const int32_t *seq_len,
+                               const int32_t *slot_map, const int64_t *slot_off,
+                               const float *k_cache, const float *v_cache, const float *q,
+                               float softmax_scale, int32_t *token_ids, int32_t *width,
+                               float *out, float *lse, qsa_timer *timer, qsa_stream stream);
 
 /* Host-only byte ledger for a cache of total_tokens tokens ([MASK] §What
  * the checkpoint measures; the dense-mask count is always 0). */

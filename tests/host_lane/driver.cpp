@@ -708,7 +708,7 @@ void test_timer() {
 
 void test_status_strings() {
   std::vector<std::string> seen;
-  for (int code = 0; code <= 6; ++code) {
+  for (int code = 0; code <= 7; ++code) {
     const char* s = qsa_status_string(code);
     CHECK(s && *s, "status %d has a string", code);
     if (s) seen.push_back(s);

@@ -39,7 +39,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     L = qsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert qsa.status_string(code)
     assert qsa.status_string(99) == "unknown status"
 

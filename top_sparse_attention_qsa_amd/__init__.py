@@ -25,6 +25,8 @@ STAGE_NAMES = ("score", "select_emit", "resolve_gather", "attend_chunks", "atten
 
 QSA_OK, QSA_ERR_NULL, QSA_ERR_SHAPE, QSA_ERR_BUDGET = 0, 1, 2, 3
 QSA_ERR_WORKSPACE, QSA_ERR_HIP, QSA_ERR_UNSUPPORTED = 4, 5, 6
+QSA_ERR_STATIC_WORKSPACE = 7
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class QSAError(RuntimeError):
@@ -105,6 +107,8 @@ def lib():
                                           ctypes.c_int),
             "qsa_decode_dedup": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, sz, P, P],
                                  ctypes.c_int),
+            "qsa_decode_noalloc": ([S, P, P, P, P, P, P, P, P, P, f32, P, P, P, P, P, P],
+                                   ctypes.c_int),
             "qsa_accounting": ([S, i64, ctypes.POINTER(Bytes)], ctypes.c_int),
             "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "qsa_version": ([], ctypes.c_char_p),
@@ -242,6 +246,23 @@ def qsa_decode(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off, 
         _ptr(lse, torch.float32, "lse", True), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), timer.handle if timer is not None else None, _stream(stream)),
         name)
+
+
+def qsa_decode_noalloc(shape, index_q, pooled, pooled_off, seq_len, slot_map, slot_off,
+                       k_cache, v_cache, q, softmax_scale, token_ids, width, out, lse, timer=None,
+                       stream=None):
+    """qsa_decode over the library's static device workspace (no workspace
+    argument, nothing allocated)."""
+    _check(lib().qsa_decode_noalloc(
+        ctypes.byref(shape), _ptr(index_q, torch.float32, "index_q"),
+        _ptr(pooled, torch.float32, "pooled"), _ptr(pooled_off, torch.int64, "pooled_off"),
+        _ptr(seq_len, torch.int32, "seq_len"), _ptr(slot_map, torch.int32, "slot_map"),
+        _ptr(slot_off, torch.int64, "slot_off"), _ptr(k_cache, torch.float32, "k_cache"),
+        _ptr(v_cache, torch.float32, "v_cache"), _ptr(q, torch.float32, "q"),
+        ctypes.c_float(softmax_scale), _ptr(token_ids, torch.int32, "token_ids"),
+        _ptr(width, torch.int32, "width"), _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse", True), timer.handle if timer is not None else None,
+        _stream(stream)), "qsa_decode_noalloc")
 
 
 def qsa_decode_fused(*args, **kw):

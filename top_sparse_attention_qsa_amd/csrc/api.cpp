@@ -136,6 +136,9 @@ const char* qsa_status_string(int status) {
     case QSA_ERR_WORKSPACE: return "workspace smaller than qsa_workspace_bytes()";
     case QSA_ERR_HIP: return "a HIP call or kernel launch failed";
     case QSA_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case QSA_ERR_STATIC_WORKSPACE:
+      return "the shape needs more workspace than the library's static buffer "
+             "(QSA_NOALLOC_WORKSPACE_BYTES); lower rows_in_flight";
     default: return "unknown status";
   }
 }
