@@ -6,6 +6,8 @@ The GPU side uses only top_sparse_attention_qsa_amd (HIP kernels); the
 expectation side uses only the CPU oracle.  Neither sees the other's results.
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -108,6 +110,68 @@ def device_kv_fetch(k_cache, v_cache):
         return (k_cache.index_select(0, idx).cpu().numpy(),
                 v_cache.index_select(0, idx).cpu().numpy())
     return fetch
+
+
+def oracle_threads():
+    """Host threads for the oracle: the cores this process may run on, at most
+    16 (the host share of one GPU on the test machines)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def oracle_rows(data, rows, kv_fetch=None, threads=None):
+    """The oracle's result for many rows, on host threads (the oracle is
+    sequential per row; its C calls release the interpreter lock).
+
+    Each sequence's raw index keys are copied to the host and pooled once; a
+    row with N visible tokens uses the first N//4 pooled groups, which is what
+    pooling its own prefix gives (a pooled group depends only on its own four
+    tokens).  K/V rows are fetched at the oracle's own resolved slots by
+    kv_fetch(slots) (default: host copies of the whole cache).  Returns one
+    dict per row, in order: n, scores, ids, slots, out_exact, lse_exact."""
+    import oracle
+    s = data["spec"]
+    threads = threads or oracle_threads()
+    raw_off = host(data["raw_off"])
+    seqs = sorted({r // s.queries for r in rows})
+    raw = {b: host(data["raw_keys"][int(raw_off[b]):int(raw_off[b]) + s.seq_lens[b]])
+           for b in seqs}
+    smap = {b: host(data["slot_map"][int(raw_off[b]):int(raw_off[b]) + s.seq_lens[b]])
+            for b in seqs}
+    qi = host(data["index_q"])
+    q = host(data["q"])
+    if kv_fetch is None:
+        kc, vc = host(data["k_cache"]), host(data["v_cache"])
+        kv_fetch = lambda slots: oracle.gather(slots, kc, vc)  # noqa: E731
+    scale = softmax_scale(s.d)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        pooled = dict(zip(seqs, ex.map(lambda b: oracle.pool_full(raw[b]), seqs)))
+
+        def select_row(r):
+            b = r // s.queries
+            n = inputs.row_tokens(s, r)
+            sc = oracle.score(qi[r], pooled[b][:max(n, 0) // 4])
+            ids = oracle.emit(oracle.select(sc, s.budget), n)
+            return dict(n=n, scores=sc, ids=ids,
+                        slots=oracle.resolve(ids, smap[b], data["kv_slots"]))
+        res = list(ex.map(select_row, rows))
+        kv = [kv_fetch(x["slots"]) for x in res]
+
+        def attend_row(i):
+            out, lse = oracle.attend_exact(q[rows[i]], kv[i][0], kv[i][1], scale)
+            res[i]["out_exact"], res[i]["lse_exact"] = out, lse
+        list(ex.map(attend_row, range(len(rows))))
+    return res
+
+
+def elementwise_rel_err(got, ref, floor=1e-6):
+    """max over elements of |got - ref| / max(|ref|, floor * max|ref| of the
+    element's output vector), in float64: the elementwise companion of
+    normwise_rel_err, with a floor so that near-zero elements do not divide
+    by ~0."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.maximum(np.abs(ref), floor * np.abs(ref).max(axis=-1, keepdims=True))
+    return float(np.max(np.abs(got - ref) / np.maximum(scale, 1e-300)))
 
 
 def normwise_rel_err(got, ref):

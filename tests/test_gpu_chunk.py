@@ -134,11 +134,27 @@ def test_full_chunk_equals_256_single_query_decodes():
     case.decode(rows="dedup")
     assert_same(case, ref)
     assert int(case.width[0]) == 2051     # boundary row: dense, 512 groups + 3 tail
+    # the oracle on 512 rows spread over all eight sequences: each sequence's
+    # first and last 16 rows and 32 rows evenly between (the 2,051-token
+    # boundary row is row 0)
+    rows = []
+    for b in range(spec.batch):
+        inner = np.linspace(16, 239, 32).round().astype(int).tolist()
+        rows += [b * 256 + j for j in list(range(16)) + inner + list(range(240, 256))]
+    assert len(rows) == 512 and 0 in rows
     fetch = harness.device_kv_fetch(case.k_cache, case.v_cache)
+    expected = harness.oracle_rows(data, rows, kv_fetch=fetch)
     ids = case.token_ids.cpu().numpy()
+    width = case.width.cpu().numpy()
     out = case.out.cpu().numpy()
-    for r in (0, 255, 256 * 3 + 17, spec.rows - 1):
-        exp = harness.oracle_row(data, r, kv_fetch=fetch)
+    worst_norm = worst_elem = 0.0
+    for r, exp in zip(rows, expected):
         w = len(exp["ids"])
+        assert width[r] == w, r
         assert np.array_equal(ids[r, :w], exp["ids"]), r
-        assert harness.normwise_rel_err(out[r], exp["out_exact"]) <= 2e-6
+        err = harness.normwise_rel_err(out[r], exp["out_exact"])
+        assert err <= 2e-6, (r, err)
+        worst_norm = max(worst_norm, err)
+        worst_elem = max(worst_elem, harness.elementwise_rel_err(out[r], exp["out_exact"]))
+    print(f"512 chunk rows: max normwise error {worst_norm:.3g}, max elementwise error "
+          f"(floor 1e-6 max|o|) {worst_elem:.3g}")
