@@ -16,7 +16,9 @@
 // hq / (H_q/H_kv)).  Scores: the chunk's K rows and query heads are staged
 // in LDS; wavefront w scores rows 16w..16w+15 for every head of the group on
 // v_mfma_f32_16x16x4_f32 (one column per head); the per-head chunk maximum is
-// exchanged once between the wavefronts.  P.V: wavefront w accumulates rows
+// exchanged once between the wavefronts (the maxima and sums over a
+// wavefront's four lane rows use the VALU cross-lane swaps, the merge's DPP
+// row rotations).  P.V: wavefront w accumulates rows
 // [w*C/NW, (w+1)*C/NW) in row order with lane = output dimension, reading its
 // V rows straight from memory (issued before the score phase); the NW
 // partial sums are then added in wavefront order.  The chunk's accumulation
@@ -420,8 +422,8 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         sc[r] = rbase + r < cn ? sacc[r] * scale : -INFINITY;
         mx = fmaxf(mx, sc[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = xor16(mx, MaxOp{});  // over the four lane rows: lq = 0..3
+      mx = xor32(mx, MaxOp{});
       if (lq == 0 && hcol) mw_sh[wave][li] = mx;
       resolve_slots(nxt2, cn_next2);
       __syncthreads();  // maxima exchanged; K no longer read, so smem can hold partials
@@ -434,8 +436,8 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = rbase + r < cn ? expf(sc[r] - m) : 0.0f;
         float l = ((p[0] + p[1]) + p[2]) + p[3];
-        l = l + __shfl_xor(l, 16, kWave);
-        l = l + __shfl_xor(l, 32, kWave);
+        l = xor16(l, AddOp{});
+        l = xor32(l, AddOp{});
         if (hcol) {
           ps4[(h * C + rbase) / 4] = make_float4(p[0], p[1], p[2], p[3]);  // read back below
           if (lq == 0) lw_sh[wave][h] = l;                                   // by this wavefront

@@ -113,6 +113,43 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Unsigned maximum over the 16 lanes of this lane's DPP row (every lane of the
+// row receives it).
+__device__ __forceinline__ uint32_t row_max16_u32(uint32_t v) {
+  uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor1, 0xF, 0xF, false);
+  v = v > y ? v : y;
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor2, 0xF, 0xF, false);
+  v = v > y ? v : y;
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor4, 0xF, 0xF, false);
+  v = v > y ? v : y;
+  y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor8, 0xF, 0xF, false);
+  return v > y ? v : y;
+}
+
+// Butterfly steps across 16-lane rows and 32-lane halves on the VALU (gfx950
+// v_permlane16_swap / v_permlane32_swap).  Swapping a value with itself
+// leaves, in every lane, the pair (x of the lane, x of the lane 16 -- resp. 32
+// -- positions away), lower-row value first in both lanes of the pair, so
+// op(first, second) gives both lanes the same bits.
+template <class Op>
+__device__ __forceinline__ float xor16(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
 __device__ __forceinline__ float wave_sum(float v) {
   v = v + dpp_f32<kRowRor1>(v);
   v = v + dpp_f32<kRowRor2>(v);

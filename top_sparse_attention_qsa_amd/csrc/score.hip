@@ -86,12 +86,8 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
   if (ok) scores[lrow * g_max + g] = s;
   if (maxima) {
     // maximum order key of the 16 consecutive groups sharing this DPP row
-    uint32_t m = ok ? order_key(s) : 0u;
-#pragma unroll
-    for (int o = kSegment / 2; o > 0; o >>= 1) {
-      const uint32_t y = (uint32_t)__shfl_xor((int)m, o, kWave);
-      m = m > y ? m : y;
-    }
+    static_assert(kSegment == 16, "one DPP row per segment");
+    const uint32_t m = row_max16_u32(ok ? order_key(s) : 0u);
     if ((lane & (kSegment - 1)) == 0 && ok) maxima[lrow * (g_max / kSegment) + g / kSegment] = m;
   }
 }
