@@ -59,14 +59,25 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive prefix sum over the wavefront's 64 lanes, on the VALU: steps of
+// 1, 2, 4 and 8 lanes inside each 16-lane DPP row (row_shr; a lane shifted in
+// from outside the row reads 0), then every row adds the totals of the rows
+// below it, read from their last lanes.  Integer sums, exact in any order.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(v, o, kWave);
-    if (lane >= o) v += y;
-  }
-  return v;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+// Value of `v` in lane `lane` (uniform across the wavefront), on the VALU.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
 // Wavefront reductions.  Within each 16-lane DPP row, rotations by 1, 2, 4

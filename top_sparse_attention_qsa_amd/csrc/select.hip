@@ -16,7 +16,8 @@
 //     order into LDS.  If more than kCandCap survive (massive ties), the
 //     passes below stream the whole row from global memory instead.
 //  3. A byte-wise radix select over the order keys finds T, the k-th largest
-//     key, and the number of keys above T.
+//     key, and the number of keys above T.  Candidates lie between tau and
+//     the row's largest key, so it starts below the bits those two share.
 //  4. An ordered pass keeps every key above T and the first (k - above)
 //     keys equal to T in position order -- the tie rule -- and writes each
 //     kept group at its output index, which is already chronological.
@@ -51,7 +52,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
   for (int it = 0; it < 2; ++it) {
     if (pending == 0) return;
     const int leader = __ffsll((unsigned long long)pending) - 1;
-    const uint32_t lb = (uint32_t)__shfl((int)bin, leader, kWave);
+    const uint32_t lb = lane_value(bin, leader);
     const uint64_t same = __ballot(active && bin == lb);
     if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
     if ((same >> lane) & 1ull) active = false;
@@ -60,11 +61,16 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
-// k-th largest order key among n keys from src (1 <= k <= n) and the count of
-// keys strictly above it: PASSES passes of 8 bits, most significant first.
-// With fewer than four passes the result is the k-th largest key with its
-// undecided low bits cleared -- a lower bound of it -- and the count is that
-// of keys above the decided prefix.
+// k-th largest order key among the n keys from src whose top `known` bits
+// equal those of `prefix0` (every key when known = 0; the caller guarantees
+// that every other key is smaller), and the count of those keys strictly
+// above it.  The next `resolve` bits are settled in 8-bit digits, most
+// significant first; a last digit that reaches below bit 0 is taken at bits
+// 0..7 instead, overlapping bits already settled, which every remaining key
+// matches.  Bits below the settled ones come back cleared: the result is then
+// a lower bound of the k-th largest key, and the count is that of keys above
+// the settled prefix.  Returns false -- after a barrier, leaving the outputs
+// unwritten -- when fewer than k keys share the known prefix.
 //
 // One barrier per pass: every wavefront finds the digit from the pass's
 // histogram itself (the same values, so the same digit), and the passes
@@ -72,19 +78,23 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 // successor was last read two passes earlier, before the previous pass's
 // barrier.  On entry no wavefront may still read sh.hist (the caller has
 // passed a barrier since the last call).
-template <class Src, int PASSES = 4>
-__device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, SelectShared& sh,
-                                  uint32_t* t_out, uint32_t* above_out) {
+template <class Src>
+__device__ bool radix_kth_largest(const Src& src, uint32_t n, uint32_t k, SelectShared& sh,
+                                  uint32_t* t_out, uint32_t* above_out, uint32_t prefix0 = 0,
+                                  int known = 0, int resolve = 32) {
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
-  uint32_t prefix = 0, mask = 0, kk = k, above = 0;
+  uint32_t mask = known > 0 ? ~0u << (32 - known) : 0u;
+  uint32_t prefix = prefix0 & mask, kk = k, above = 0;
+  const int passes = (resolve + 7) / 8;
   for (int i = tid; i < 256; i += NT) sh.hist[0][i] = 0;
   __syncthreads();
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int shift = 24 - 8 * p;
+#pragma unroll 1
+  for (int p = 0; p < passes; ++p) {
+    const int top = 32 - known - 8 * p;          // bits >= top are settled
+    const int shift = top > 8 ? top - 8 : 0;
     uint32_t* hist = sh.hist[p % 3];
-    if (p + 1 < PASSES)
+    if (p + 1 < passes)
       for (int i = tid; i < 256; i += NT) sh.hist[(p + 1) % 3][i] = 0;
     const uint32_t n_up = (n + NT - 1) / NT * NT;   // whole wavefronts stay converged
     for (uint32_t i = tid; i < n_up; i += NT) {
@@ -102,13 +112,14 @@ __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, Select
     // finds the digit, which every lane then reads from it
     const uint4 h = *reinterpret_cast<const uint4*>(hist + 4 * lane);
     const uint32_t mine = (h.x + h.y) + (h.z + h.w);
-    uint32_t suffix = mine;  // sum over lanes >= l
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_down((int)suffix, o, kWave);
-      if (lane + o < kWave) suffix += y;
+    const uint32_t inc = wave_inclusive_sum(mine);  // lanes <= l
+    const uint32_t total = lane_value(inc, kWave - 1);
+    if (p == 0 && total < kk) {
+      __syncthreads();  // every wavefront is done reading this histogram
+      return false;
     }
-    const uint32_t higher = suffix - mine;  // keys in bins above lane l's
+    const uint32_t higher = total - inc;    // keys in bins above lane l's
+    const uint32_t suffix = higher + mine;  // keys in lane l's bins and above
     const bool owner = higher < kk && kk <= suffix;
     uint32_t acc = higher, digit = 4u * (uint32_t)lane;
     const uint32_t hb[4] = {h.x, h.y, h.z, h.w};
@@ -122,8 +133,8 @@ __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, Select
       if (!found) acc += hb[b];
     }
     const int src_lane = __ffsll((unsigned long long)__ballot(owner)) - 1;
-    digit = (uint32_t)__shfl((int)digit, src_lane, kWave);
-    acc = (uint32_t)__shfl((int)acc, src_lane, kWave);
+    digit = lane_value(digit, src_lane);
+    acc = lane_value(acc, src_lane);
     above += acc;
     kk -= acc;
     prefix |= digit << shift;
@@ -131,6 +142,7 @@ __device__ void radix_kth_largest(const Src& src, uint32_t n, uint32_t k, Select
   }
   *t_out = prefix;
   *above_out = above;
+  return true;
 }
 
 struct GlobalScores {
@@ -226,7 +238,8 @@ constexpr int kSegRounds = 16;  // 64-score rounds per wavefront in one pass
 
 __device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ srow,
                                    const uint32_t* __restrict__ mrow, uint32_t G, uint32_t segs,
-                                   uint32_t k, uint32_t* n_cand, bool* overflow) {
+                                   uint32_t k, uint32_t* n_cand, bool* overflow,
+                                   uint32_t* tau_out, uint32_t* top_out) {
   const int tid = (int)threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
@@ -255,9 +268,33 @@ __device__ bool segment_candidates(SelectShared& sh, const float* __restrict__ s
     for (int e = 0; e < 4; ++e)
       if (s0 + e < nf) sh.maxima[s0 + e] = mx[e];
   }
+  // the row's largest key, the largest segment maximum (sh.wave_tot is free
+  // until the listing below)
+  {
+    const uint32_t a = mx[0] > mx[1] ? mx[0] : mx[1], b = mx[2] > mx[3] ? mx[2] : mx[3];
+    const uint32_t r = row_max16_u32(a > b ? a : b);
+    // readlane returns int: compare the lanes' keys as unsigned
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)r, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)r, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)r, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)r, 48);
+    const uint32_t r01 = r0 > r1 ? r0 : r1, r23 = r2 > r3 ? r2 : r3;
+    if (lane == 0) sh.wave_tot[wave] = r01 > r23 ? r01 : r23;
+  }
   __syncthreads();
+  uint32_t top = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) top = top > sh.wave_tot[w] ? top : sh.wave_tot[w];
+  // tau: the k-th largest maximum to 17 bits in one pass, among the maxima
+  // sharing the largest one's sign and exponent (9 bits) -- all maxima
+  // outside that binade are smaller; or, when fewer than k share it, to 16
+  // bits in two passes over all of them.  Either way a lower bound of the
+  // k-th largest maximum.
   uint32_t tau, above_unused;
-  radix_kth_largest<LdsCands, 2>(LdsCands{sh.maxima}, nf, k, sh, &tau, &above_unused);
+  if (!radix_kth_largest(LdsCands{sh.maxima}, nf, k, sh, &tau, &above_unused, top, 9, 8))
+    radix_kth_largest(LdsCands{sh.maxima}, nf, k, sh, &tau, &above_unused, 0u, 0, 16);
+  *tau_out = tau;
+  *top_out = top;
 
   // this wavefront's list of segments reaching tau (in sh.maxima, 256 per
   // wavefront, after the radix select is done with it)
@@ -371,11 +408,12 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     uint32_t n_cand = 0;
     bool overflow = false;
     bool compacted = false;  // candidates already in LDS (segment-skipping pass)
+    uint32_t tau = 0, top = 0;  // with compacted: every candidate key is in [tau, top]
     const uint32_t segs = (G + kSegment - 1) / kSegment;
     if constexpr (!P::kCertified) {
       if (maxima && segs >= (uint32_t)k && segs <= 4u * NT)
         compacted = segment_candidates(sh, srow, maxima + lrow * (g_max / kSegment), G, segs,
-                                       (uint32_t)k, &n_cand, &overflow);
+                                       (uint32_t)k, &n_cand, &overflow, &tau, &top);
     }
     if (!compacted) {
     // 1. threshold bound from the segment maxima, staged once in LDS.  While
@@ -383,7 +421,7 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     //    (their maximum): still one maximum per disjoint set of groups, so the
     //    k-th largest of the folded values is still a lower bound of the k-th
     //    largest score, and the radix select works on fewer values.
-    uint32_t tau = 0;
+    tau = 0;
     if (maxima && segs >= (uint32_t)k) {
       const uint32_t* mrow = maxima + lrow * (g_max / kSegment);
       uint32_t f = 1;
@@ -489,10 +527,16 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     //    on the fly for certified rows)
     uint32_t T, above;
     const uint32_t n_src = overflow ? G : n_cand;
-    if (overflow)
+    if (overflow) {
       radix_kth_largest(FullKeys<P>{&pol}, G, (uint32_t)k, sh, &T, &above);
-    else
+    } else if (compacted) {
+      // the candidates share the bits that tau and the row's largest key share
+      const int known = tau == top ? 32 : __clz(tau ^ top);
+      radix_kth_largest(LdsCands{sh.cand_key}, n_cand, (uint32_t)k, sh, &T, &above, top, known,
+                        32 - known);
+    } else {
       radix_kth_largest(LdsCands{sh.cand_key}, n_cand, (uint32_t)k, sh, &T, &above);
+    }
     const uint32_t need = (uint32_t)k - above;  // keys equal to T to keep, lowest positions first
 
     // 4. ordered keep pass: 4 consecutive entries per thread per round
