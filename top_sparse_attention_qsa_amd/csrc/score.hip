@@ -9,20 +9,173 @@
 //
 // Mapping: one lane owns one group and a wavefront owns one pooled-key tile of
 // 64 groups; in the tiled layout, dimension chunk c of a tile is 1 KiB
-// contiguous, so each float4 load of the wave is one coalesced 1 KiB read.  The index query is uniform across the workgroup and is read
-// with scalar loads into SGPRs, so the fma operand costs no LDS or VALU work.
+// contiguous, so each float4 load of the wave is one coalesced 1 KiB read.
+// With 4, 8 or 16 index heads the multiply-adds run on the matrix cores
+// (score_mfma_kernel: v_mfma_f32_4x4x1_16b_f32 rounds each step once, like
+// fmaf, so the bits are those of the chain); the query row is staged in LDS.
+// With 1 or 2 heads they run on the VALU (score_kernel), the query in SGPRs.
 // The workload is HBM-bound: 8 flop per pooled-key byte.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-// Pooled keys are read once per step, so they are loaded with the
-// nontemporal hint and do not displace the scores or other live data in L2.
-__device__ __forceinline__ float4 load_stream(const float* p) {
-  typedef float v4 __attribute__((ext_vector_type(4)));
-  const v4 v = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
+// Cache-policy operand of the buffer intrinsics on this architecture: bit 0
+// sc0, bit 1 nt, bit 4 sc1.
+constexpr int kPolicyNt = 2;
+
+// A raw buffer resource over `bytes` bytes at p (a uniform address).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                           (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
+// Chunk c (dimensions 4c..4c+3) of this lane's group in a wavefront's tile.
+// Pooled keys are read once per step, so the loads carry the nontemporal
+// hint; every offset lies inside the tile (no SGPR offset: that part of a
+// buffer address is not range checked).
+struct TileLoader {
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ float4 operator()(int c, int lane) const {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 v = __builtin_bit_cast(
+        v4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + c * 1024, 0, kPolicyNt));
+    return make_float4(v.x, v.y, v.z, v.w);
+  }
+};
+
+// Stores of a wavefront's 64 scores (lane l: group g) and of its tile's four
+// 16-group segment maxima (mk: the maximum order key of the lane's DPP row),
+// the maxima as one 16-byte store from lane 0; segments past the row's last
+// group hold 0 there, and are never read.  Both are nontemporal: in a
+// load-only probe of this kernel's reads, plain 256-byte score stores per
+// wavefront added 5-10 us to the 163 us read of 1 GiB, nontemporal ones about
+// 1 us (in the decode step the gain is 0-4 us, depending on the device).
+__device__ __forceinline__ void store_scores(float* __restrict__ srow, uint32_t* __restrict__ mrow,
+                                             int64_t g_max, int64_t g, bool ok, float s,
+                                             uint32_t mk) {
+  const int lane = lane_id();
+  const auto srs = buffer_over(srow, (uint32_t)(g_max * 4));
+  if (ok) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), srs, (int)(g * 4), 0,
+                                                kPolicyNt);
+  if (mrow) {
+    const auto mrs = buffer_over(mrow, (uint32_t)((g_max / kSegment) * 4));
+    const uint32_t m1 = lane_value(mk, 16), m2 = lane_value(mk, 32), m3 = lane_value(mk, 48);
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    if (lane == 0 && ok)
+      __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)mk, (int)m1, (int)m2, (int)m3}, mrs,
+                                             (int)((g / kSegment) * 4), 0, kPolicyNt);
+  }
+}
+
+// Matrix-core form of score_kernel for HI a multiple of 4: the same lanes,
+// loads and fused multiply-adds in the same order, issued as
+// v_mfma_f32_4x4x1_16b_f32.  With one product per step, block b of that
+// instruction (lanes 4b..4b+3) adds A[i] * B[j] to D[i][j] with one
+// rounding, A[i] from lane 4b+i and B[j] from lane 4b+j, D[i][j] in
+// register i of lane 4b+j: with B = the key value of group l in lane l and
+// A = the query value of head 4m + (l mod 4), register i of lane l
+// accumulates head 4m+i of group l exactly as the fmaf chain does.
+template <int HI, int DI>
+__global__ void __launch_bounds__(kScoreWaves * kWave)
+score_mfma_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled,
+                  const int64_t* __restrict__ pooled_off, const int32_t* __restrict__ seq_len,
+                  int32_t queries, int64_t g_max, int64_t row0, float* __restrict__ scores,
+                  uint32_t* __restrict__ maxima) {
+  static_assert(HI % 4 == 0, "head quads");
+  constexpr int HQ = HI / 4;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef float vqf __attribute__((ext_vector_type(HQ)));
+  const int64_t lrow = blockIdx.y;
+  const int64_t row = row0 + lrow;
+  const RowView rv = row_view(seq_len, row, queries, g_max);
+  if (!rv.valid) return;
+  const int wave = (int)(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int64_t tile = (int64_t)blockIdx.x * kScoreWaves + wave;  // 64 groups per wavefront
+  const bool active = tile * 64 < rv.g;
+
+  const float* __restrict__ qrow = index_q + row * (int64_t)(HI * DI);
+  const float* tbase = pooled + pooled_off[rv.b] + tile * (64 * DI);
+  const TileLoader ld{buffer_over(tbase, 64 * DI * 4)};
+
+  constexpr int NC = DI / 4;
+  constexpr int PF = 2;  // the same ring as score_kernel
+  static_assert(NC % PF == 0, "ring depth must divide the chunk count");
+  float4 ring[PF];
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) ring[u] = ld(u, lane);
+  }
+  // the row's query, dimension-major: qs[d][i] holds heads i, 4+i, 8+i, ...
+  __shared__ __attribute__((aligned(16))) float qs[DI][4][HQ];
+  {
+    constexpr int NT = kScoreWaves * kWave;
+    constexpr int QV = HI * DI / 4;  // float4 of the query row
+    constexpr int PER = (QV + NT - 1) / NT;
+    float4 qv[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e4 = (int)threadIdx.x + p * NT;
+      if (QV % NT == 0 || e4 < QV) qv[p] = reinterpret_cast<const float4*>(qrow)[e4];
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e4 = (int)threadIdx.x + p * NT;
+      if (QV % NT == 0 || e4 < QV) {
+        const int h = (4 * e4) / DI, d = 4 * e4 - h * DI;
+        qs[d + 0][h & 3][h >> 2] = qv[p].x;
+        qs[d + 1][h & 3][h >> 2] = qv[p].y;
+        qs[d + 2][h & 3][h >> 2] = qv[p].z;
+        qs[d + 3][h & 3][h >> 2] = qv[p].w;
+      }
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+
+  v4f acc[HQ];
+#pragma unroll
+  for (int m = 0; m < HQ; ++m) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const int qi = lane & 3;
+
+#pragma unroll 1
+  for (int cb = 0; cb < NC; cb += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int c = cb + u;
+      const float4 kv = ring[u];
+      if (c + PF < NC) ring[u] = ld(c + PF, lane);
+      const vqf a0 = *reinterpret_cast<const vqf*>(&qs[4 * c + 0][qi][0]);
+      const vqf a1 = *reinterpret_cast<const vqf*>(&qs[4 * c + 1][qi][0]);
+      const vqf a2 = *reinterpret_cast<const vqf*>(&qs[4 * c + 2][qi][0]);
+      const vqf a3 = *reinterpret_cast<const vqf*>(&qs[4 * c + 3][qi][0]);
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0[m], kv.x, acc[m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1[m], kv.y, acc[m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a2[m], kv.z, acc[m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a3[m], kv.w, acc[m], 0, 0, 0);
+    }
+  }
+
+  float s = 0.0f;
+#pragma unroll
+  for (int m = 0; m < HQ; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = s + (acc[m][i] > 0.0f ? acc[m][i] : 0.0f);
+  const int64_t g = tile * 64 + lane;
+  const bool ok = g < rv.g;
+  static_assert(kSegment == 16, "one DPP row per segment");
+  const uint32_t mk = maxima ? row_max16_u32(ok ? order_key(s) : 0u) : 0u;
+  store_scores(scores + lrow * g_max, maxima ? maxima + lrow * (g_max / kSegment) : nullptr,
+               g_max, g, ok, s, mk);
 }
 
 template <int HI, int DI>
@@ -41,7 +194,8 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
   if (tile * 64 >= rv.g) return;
 
   const float* __restrict__ qrow = index_q + row * (int64_t)(HI * DI);
-  const float* __restrict__ kbase = pooled + pooled_off[rv.b] + tile * (64 * DI) + lane * 4;
+  const float* tbase = pooled + pooled_off[rv.b] + tile * (64 * DI);
+  const TileLoader ld{buffer_over(tbase, 64 * DI * 4)};
 
   float acc[HI];
 #pragma unroll
@@ -56,7 +210,7 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
   static_assert(NC % PF == 0, "ring depth must divide the chunk count");
   float4 ring[PF];
 #pragma unroll
-  for (int u = 0; u < PF; ++u) ring[u] = load_stream(kbase + u * 256);
+  for (int u = 0; u < PF; ++u) ring[u] = ld(u, lane);
 
 #pragma unroll 1
   for (int cb = 0; cb < NC; cb += PF) {
@@ -64,7 +218,7 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
     for (int u = 0; u < PF; ++u) {
       const int c = cb + u;
       const float4 kv = ring[u];
-      if (c + PF < NC) ring[u] = load_stream(kbase + (c + PF) * 256);
+      if (c + PF < NC) ring[u] = ld(c + PF, lane);
       const float* __restrict__ qc = qrow + 4 * c;
 #pragma unroll
       for (int h = 0; h < HI; ++h) {
@@ -83,13 +237,11 @@ score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled
   for (int h = 0; h < HI; ++h) s = s + (acc[h] > 0.0f ? acc[h] : 0.0f);
   const int64_t g = tile * 64 + lane;
   const bool ok = g < rv.g;
-  if (ok) scores[lrow * g_max + g] = s;
-  if (maxima) {
-    // maximum order key of the 16 consecutive groups sharing this DPP row
-    static_assert(kSegment == 16, "one DPP row per segment");
-    const uint32_t m = row_max16_u32(ok ? order_key(s) : 0u);
-    if ((lane & (kSegment - 1)) == 0 && ok) maxima[lrow * (g_max / kSegment) + g / kSegment] = m;
-  }
+  // maximum order key of the 16 consecutive groups sharing this DPP row
+  static_assert(kSegment == 16, "one DPP row per segment");
+  const uint32_t mk = maxima ? row_max16_u32(ok ? order_key(s) : 0u) : 0u;
+  store_scores(scores + lrow * g_max, maxima ? maxima + lrow * (g_max / kSegment) : nullptr,
+               g_max, g, ok, s, mk);
 }
 
 __global__ void __launch_bounds__(256)
@@ -119,9 +271,14 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int64_t tiles = (a.g_max + 63) / 64;
   dim3 grid((unsigned)((tiles + kScoreWaves - 1) / kScoreWaves), (unsigned)a.rows);
   if (grid.x == 0 || a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((score_kernel<HI, DI>), grid,
-                     dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
-                     a.seq_len, a.queries, a.g_max, a.row0, a.scores, a.maxima);
+  if constexpr (HI % 4 == 0)
+    hipLaunchKernelGGL((score_mfma_kernel<HI, DI>), grid,
+                       dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
+                       a.seq_len, a.queries, a.g_max, a.row0, a.scores, a.maxima);
+  else
+    hipLaunchKernelGGL((score_kernel<HI, DI>), grid,
+                       dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
+                       a.seq_len, a.queries, a.g_max, a.row0, a.scores, a.maxima);
   return hipGetLastError();
 }
 
