@@ -671,7 +671,7 @@ def main():
         "step_traffic": step_traffic,
         "context_bandwidth": context,
         "roofline": {
-            "kernel": "score_kernel<16,128>",
+            "kernel": "score_mfma_kernel<16,128>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
