@@ -114,24 +114,29 @@ score_mfma_kernel(const float* __restrict__ index_q, const float* __restrict__ p
   // the row's query, dimension-major: qs[d][i] holds heads i, 4+i, 8+i, ...
   __shared__ __attribute__((aligned(16))) float qs[DI][4][HQ];
   {
+    // thread t fills entry t = (d, i) of qs with heads i, 4+i, ...: its HQ
+    // values are gathered from the query rows, and consecutive threads write
+    // consecutive entries (no LDS bank conflicts)
     constexpr int NT = kScoreWaves * kWave;
-    constexpr int QV = HI * DI / 4;  // float4 of the query row
-    constexpr int PER = (QV + NT - 1) / NT;
-    float4 qv[PER];
+    constexpr int NE = DI * 4;  // (d, i) entries
+    constexpr int PER = (NE + NT - 1) / NT;
+    float qv[PER][HQ];
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e4 = (int)threadIdx.x + p * NT;
-      if (QV % NT == 0 || e4 < QV) qv[p] = reinterpret_cast<const float4*>(qrow)[e4];
+      const int e = (int)threadIdx.x + p * NT;
+      const int d = e >> 2, i = e & 3;
+#pragma unroll
+      for (int m = 0; m < HQ; ++m)
+        if (NE % NT == 0 || e < NE) qv[p][m] = qrow[(4 * m + i) * DI + d];
     }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e4 = (int)threadIdx.x + p * NT;
-      if (QV % NT == 0 || e4 < QV) {
-        const int h = (4 * e4) / DI, d = 4 * e4 - h * DI;
-        qs[d + 0][h & 3][h >> 2] = qv[p].x;
-        qs[d + 1][h & 3][h >> 2] = qv[p].y;
-        qs[d + 2][h & 3][h >> 2] = qv[p].z;
-        qs[d + 3][h & 3][h >> 2] = qv[p].w;
+      const int e = (int)threadIdx.x + p * NT;
+      if (NE % NT == 0 || e < NE) {
+        vqf v;
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) v[m] = qv[p][m];
+        *reinterpret_cast<vqf*>(&qs[e >> 2][e & 3][0]) = v;
       }
     }
   }
