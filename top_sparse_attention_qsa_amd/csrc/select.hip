@@ -199,6 +199,72 @@ struct CertifiedScores {
     return order_key(sc);
   }
   __device__ uint32_t full_key(uint32_t g) const { return exact_key(g); }
+
+  // Exact keys of the n compacted candidates, written over their bounds: a
+  // wavefront takes 64 candidates at a time, lane = candidate, and runs the
+  // chain on v_mfma_f32_4x4x1_16b_f32 exactly as score.hip does (one
+  // rounding per step, so the bits are those of exact_key).  The query row is
+  // staged in `qs` (LDS scratch of DI * HI floats, dimension-major: entry
+  // (d, i) holds heads i, 4+i, ...).  Called by the whole workgroup.
+  __device__ void rescore_all(uint32_t* cand_key, const uint32_t* cand_pos, uint32_t n,
+                              float* qs) const {
+    static_assert(HI % 4 == 0, "head quads");
+    constexpr int HQ = HI / 4;
+    constexpr int NC = DI / 4;
+    // a candidate's key is 32 pieces of 16 B, 1 KiB apart in the tiled layout:
+    // up to 16 gathers in flight per lane (4 in flight: 210 us of rescoring
+    // per causal-chunk leg, 16: 188 us, against 253 us for one chain per
+    // thread on the VALU)
+    constexpr int PF = 16 < NC ? 16 : NC;
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef float vqf __attribute__((ext_vector_type(HQ)));
+    const int tid = (int)threadIdx.x;
+    for (int e = tid; e < DI * 4; e += NT) {
+      const int d = e >> 2, i = e & 3;
+      vqf v;
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) v[m] = q[(4 * m + i) * DI + d];
+      *reinterpret_cast<vqf*>(qs + e * HQ) = v;
+    }
+    __syncthreads();
+    const int lane = lane_id();
+    const int qi = lane & 3;
+    for (uint32_t base = 64u * (uint32_t)wave_id(); base < n; base += 64u * NWAVES) {
+      const uint32_t c_i = base + (uint32_t)lane;
+      const bool valid = c_i < n;
+      const uint32_t g = cand_pos[valid ? c_i : 0u];  // n >= 1: lanes past n reread entry 0
+      const float* kb = kp + (int64_t)(g >> 6) * (64 * DI) + (g & 63) * 4;
+      float4 ring[PF];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) ring[u] = *reinterpret_cast<const float4*>(kb + u * 256);
+      v4f acc[HQ];
+#pragma unroll
+      for (int m = 0; m < HQ; ++m) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float4 kv = ring[c % PF];
+        if (c + PF < NC) ring[c % PF] = *reinterpret_cast<const float4*>(kb + (c + PF) * 256);
+        const vqf a0 = *reinterpret_cast<const vqf*>(qs + ((4 * c + 0) * 4 + qi) * HQ);
+        const vqf a1 = *reinterpret_cast<const vqf*>(qs + ((4 * c + 1) * 4 + qi) * HQ);
+        const vqf a2 = *reinterpret_cast<const vqf*>(qs + ((4 * c + 2) * 4 + qi) * HQ);
+        const vqf a3 = *reinterpret_cast<const vqf*>(qs + ((4 * c + 3) * 4 + qi) * HQ);
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0[m], kv.x, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1[m], kv.y, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a2[m], kv.z, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < HQ; ++m) acc[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(a3[m], kv.w, acc[m], 0, 0, 0);
+      }
+      float sc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < HQ; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc = sc + (acc[m][i] > 0.0f ? acc[m][i] : 0.0f);
+      if (valid) cand_key[c_i] = order_key(sc);
+    }
+  }
 };
 
 template <class P>
@@ -515,9 +581,11 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     }  // !compacted
     __syncthreads();
     if constexpr (P::kCertified) {
-      // the candidates' bounds are replaced by their exact (chain) keys
+      // the candidates' bounds are replaced by their exact (chain) keys; the
+      // query row is staged over the segment maxima, which are no longer read
       if (!overflow) {
-        for (uint32_t i = tid; i < n_cand; i += NT) sh.cand_key[i] = pol.exact_key(sh.cand_pos[i]);
+        static_assert(sizeof(SelectShared::maxima) >= sizeof(float) * 16 * 128, "query staging");
+        pol.rescore_all(sh.cand_key, sh.cand_pos, n_cand, reinterpret_cast<float*>(sh.maxima));
         __syncthreads();
       }
     }
