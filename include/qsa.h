@@ -242,7 +242,8 @@ QSA_API void qsa_timer_destroy(qsa_timer *timer);
  * qsa_score_groups_chunk supports, step 1 runs on MFMA with certified bounds
  * and the candidates are rescored exactly, so every row's result equals a
  * decode of that row alone.  Workspace >= qsa_workspace_bytes(shape)
- * holds scores, maxima, compact K/V and attention partials.  timer may be
+ * holds scores, maxima, tile error widths (causal chunks), compact K/V
+ * and attention partials.  timer may be
  * NULL.  Intermediate scratch contents are undefined after the call. */
 QSA_API int qsa_decode(const qsa_shape *shape, const float *index_q, const float *pooled,
                const int64_t *pooled_off, const int32_t *seq_len, const int32_t *slot_map,

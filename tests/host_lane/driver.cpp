@@ -131,7 +131,8 @@ void expect_rejected(DecodeFn f, const DecodeCall& c, int code, const char* what
 }
 
 // Workspace regions of one pass, recomputed from the layout's definition:
-// scores, maxima, compact K, compact V, partial accumulators, partial (m, l).
+// scores, maxima, compact K, compact V, partial accumulators, partial (m, l),
+// and for causal-chunk rows the tile widths of the certified selection.
 struct Region {
   const char* name;
   uintptr_t begin, bytes;
@@ -149,6 +150,7 @@ std::vector<Region> expected_regions(const qsa_shape& s) {
   r.push_back({"v_compact", 0, (uintptr_t)(R * stride * s.kv_heads * s.head_dim * 4)});
   r.push_back({"part_acc", 0, (uintptr_t)(R * s.q_heads * chunks * s.head_dim * 4)});
   r.push_back({"part_ml", 0, (uintptr_t)(R * s.q_heads * chunks * 2 * 4)});
+  r.push_back({"widths", 0, (uintptr_t)(R * (s.max_groups / 64) * 4)});
   return r;
 }
 
@@ -179,6 +181,8 @@ void check_decode_chain(const Named& d, const qsa_shape& s, bool chunk) {
   const stub::Call& att = stub::calls[stages.size() - 2];
   reg[4].begin = (uintptr_t)att.ptrs[4];
   reg[5].begin = (uintptr_t)att.ptrs[5];
+  Region widths = reg[6];
+  reg.pop_back();
   size_t nreg = 2;
   if (d.rows_stage && std::string(d.rows_stage) == "gather") {
     reg[2].begin = (uintptr_t)stub::calls[2].ptrs[7];
@@ -191,6 +195,12 @@ void check_decode_chain(const Named& d, const qsa_shape& s, bool chunk) {
   } else {
     reg.erase(reg.begin() + 2, reg.begin() + 4);
     nreg = 4;
+  }
+  if (chunk) {  // the chunk launch passes its segment widths as ptr 6
+    widths.begin = (uintptr_t)c0.ptrs[6];
+    reg.insert(reg.begin() + nreg, widths);
+    ++nreg;
+    CHECK(stub::calls[1].ptrs[6] == c0.ptrs[6], "%s: selection reads the chunk's widths", d.name);
   }
   for (size_t i = 0; i < nreg; ++i) {
     CHECK(in_ws((void*)reg[i].begin), "%s: %s outside the workspace", d.name, reg[i].name);

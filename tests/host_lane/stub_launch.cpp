@@ -78,11 +78,12 @@ int launch_dense_ids(const int32_t* seq_len, int32_t, int32_t, int64_t rows, int
 }
 int launch_chunk(const ChunkArgs& a, int, int, void* s) {
   return stub::record("chunk", a.row0, a.rows,
-                      {a.index_q, a.pooled, a.approx, a.bound, a.hi, a.lo_maxima}, s);
+                      {a.index_q, a.pooled, a.approx, a.bound, a.hi, a.lo_maxima, a.widths}, s);
 }
 int launch_select_certified(const SelectArgs& a, const RescoreArgs& r, void* s) {
   return stub::record("select_certified", a.row0, a.rows,
-                      {a.scores, a.maxima, a.token_ids, a.width, r.index_q, r.pooled}, s);
+                      {a.scores, a.maxima, a.token_ids, a.width, r.index_q, r.pooled, a.widths},
+                      s);
 }
 int launch_union(const UnionArgs& a, void* s) {
   return stub::record("union", a.row0, a.rows,

@@ -59,9 +59,10 @@ def test_workspace_scales_with_groups_and_width_never_tokens():
     measures)."""
     base = qsa.qsa_workspace_bytes(shape())
     assert base > 0
-    # per row: scores (4 B/group) + maxima (4 B / 16 groups) + compact K/V + partials
+    # per row: scores (4 B/group) + maxima (4 B / 16 groups) + tile widths
+    # (4 B / 64 groups) + compact K/V + partials
     per_row_compact = 2 * (4 * 512 + 4) * 4 * 128 * 4
-    per_row_groups = 65536 * 4 + 65536 // 16 * 4
+    per_row_groups = 65536 * 4 + 65536 // 16 * 4 + 65536 // 64 * 4
     per_row_part = 32 * 33 * (128 + 2) * 4
     # union gather: row bitmap, union bitmap and word prefixes (at most one
     # sequence per row), union list, position list

@@ -70,7 +70,7 @@ int validate(const qsa_shape* s, int need) {
 }
 
 struct Layout {
-  size_t scores, maxima, kc, vc, pacc, pml;
+  size_t scores, maxima, widths, kc, vc, pacc, pml;
   size_t rbm, ubm, upre, ublk, ulist, upos;  // union gather (chunk dedup)
   size_t total;
 };
@@ -84,6 +84,8 @@ Layout layout(const qsa_shape* s) {
   off = align256(off + (size_t)R * g * sizeof(float));
   L.maxima = off;
   off = align256(off + (size_t)R * (g / kSegment) * sizeof(uint32_t));
+  L.widths = off;  // certified (causal chunk) rows only: one per 64-group tile
+  off = align256(off + (size_t)R * (g / 64) * sizeof(float));
   const size_t compact = (size_t)R * token_stride(s) * s->kv_heads * s->head_dim * sizeof(float);
   L.kc = off;
   off = align256(off + compact);
@@ -399,6 +401,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
   char* w = (char*)ws;
   float* scores = reinterpret_cast<float*>(w + L.scores);
   uint32_t* maxima = reinterpret_cast<uint32_t*>(w + L.maxima);
+  float* widths = reinterpret_cast<float*>(w + L.widths);
   float* kc = reinterpret_cast<float*>(w + L.kc);
   float* vc = reinterpret_cast<float*>(w + L.vc);
   float* pacc = reinterpret_cast<float*>(w + L.pacc);
@@ -424,7 +427,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
     if (!record(0)) return QSA_ERR_HIP;
     if (chunk) {
       ChunkArgs ca{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
-                   nullptr, nullptr, scores, maxima};
+                   nullptr, nullptr, scores, maxima, widths};
       if (launch_chunk(ca, s->index_heads, s->index_dim, st) != 0) return QSA_ERR_HIP;
     } else {
       ScoreArgs sa{index_q, pooled, pooled_off, seq_len, s->queries, s->max_groups, r0, n,
@@ -435,6 +438,7 @@ static int decode_impl(Rows mode, const qsa_shape* s, const float* index_q, cons
     SelectArgs se{scores, maxima, seq_len, s->queries, s->max_groups, s->budget_groups,
                   r0, n, nullptr, token_ids, width};
     if (chunk) {
+      se.widths = widths;
       RescoreArgs ra{index_q, pooled, pooled_off, s->index_heads, s->index_dim};
       if (launch_select_certified(se, ra, st) != 0) return QSA_ERR_HIP;
     } else if (launch_select(se, st) != 0) {

@@ -49,7 +49,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
                    const int64_t* __restrict__ pooled_off, const int32_t* __restrict__ seq_len,
                    int32_t queries, int64_t g_max, int64_t row0, float* __restrict__ approx,
                    float* __restrict__ bound, float* __restrict__ hi,
-                   uint32_t* __restrict__ lo_maxima) {
+                   uint32_t* __restrict__ lo_maxima, float* __restrict__ widths) {
   constexpr int RPM = 16 / HI;    // query rows per M-tile
   constexpr int RB = 4 * RPM;     // query rows per workgroup
   constexpr int NQ = DI / 16;     // quads of four k-steps
@@ -172,12 +172,14 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   constexpr float gD2 = (DI + 2) * u / (1.0f - (DI + 2) * u);
   constexpr float gH = HI * u / (1.0f - HI * u);
   const int sub_row = (4 * (lane >> 4)) / HI;  // row within the M-tile held by this lane
+  float wt[4] = {0.0f, 0.0f, 0.0f, 0.0f};      // per M-tile: the widest group of the tile
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     // |k_g|^2: lanes l, l^16, l^32, l^48 hold the four k-lanes of group l%16
+    // (VALU cross-lane swaps: both lanes of a pair add the same two values)
     float kk = ksq[t];
-    kk += __shfl_xor(kk, 16, kWave);
-    kk += __shfl_xor(kk, 32, kWave);
+    kk = xor16(kk, AddOp{});
+    kk = xor32(kk, AddOp{});
     const float knorm = sqrtf(kk);
     const int64_t g = tile * 64 + t * 16 + (lane & 15);
 #pragma unroll
@@ -186,8 +188,8 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
       const f32x4 d = acc[m][t];
       float s = (d.x > 0.f ? d.x : 0.f) + (d.y > 0.f ? d.y : 0.f) + (d.z > 0.f ? d.z : 0.f) +
                 (d.w > 0.f ? d.w : 0.f);
-#pragma unroll
-      for (int o = 16; o < 4 * HI; o <<= 1) s += __shfl_xor(s, o, kWave);
+      if constexpr (HI >= 8) s = xor16(s, AddOp{});  // the head sum across lane rows
+      if constexpr (HI >= 16) s = xor32(s, AddOp{});
       const int r = m * RPM + sub_row;
       int64_t g_row = g_rows[m * RPM];  // select, not a lane-dependent register index
 #pragma unroll
@@ -205,15 +207,31 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
         if (hi) hi[lr * g_max + g] = s + e;
       }
       if (lo_maxima) {
-        uint32_t mk = ok ? order_key(s - e) : 0u;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const uint32_t y = (uint32_t)__shfl_xor((int)mk, o, kWave);
-          mk = mk > y ? mk : y;
-        }
+        // segment = the 16 lanes of a DPP row
+        const uint32_t mk = row_max16_u32(ok ? order_key(s - e) : 0u);
         if (writer && (lane & 15) == 0 && ok)
           lo_maxima[lr * (g_max / kSegment) + g / kSegment] = mk;
       }
+      // hi - s <= (s~ + e)(1 + u) - (s~ - e/2) < 1.5e + u|hi|; the width adds
+      // margin for its own rounding and for the subtraction hi - W the
+      // selection makes, so that fl(hi - W) <= s (select.hip, certified band)
+      if (ok) wt[m] = fmaxf(wt[m], 2.02f * e + 4.0f * u * fabsf(s + e));
+    }
+  }
+  if (widths) {
+    // one width per (row, 64-group tile): the maximum over the DPP row of the
+    // lanes' maxima over the four N-subtiles (all 64 groups of the tile)
+    const bool writer = ((lane >> 4) % (HI / 4)) == 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float w = row_max16(wt[m]);
+      const int r = m * RPM + sub_row;
+      int64_t g_row = g_rows[m * RPM];
+#pragma unroll
+      for (int q2 = 1; q2 < RPM; ++q2)
+        if (sub_row == q2) g_row = g_rows[m * RPM + q2];
+      if (writer && (lane & 15) == 0 && tile * 64 < g_row)
+        widths[(lrow0 + r) * (g_max / 64) + tile] = w;
     }
   }
 }
@@ -226,7 +244,7 @@ hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_score_kernel<HI, DI>), grid, dim3(4 * kWave), 0, s, a.index_q,
                      a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0, a.approx,
-                     a.bound, a.hi, a.lo_maxima);
+                     a.bound, a.hi, a.lo_maxima, a.widths);
   return hipGetLastError();
 }
 

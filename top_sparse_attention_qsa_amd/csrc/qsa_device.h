@@ -137,6 +137,18 @@ __device__ __forceinline__ uint32_t row_max16_u32(uint32_t v) {
   return v > y ? v : y;
 }
 
+// Unsigned sum and maximum over the wavefront; every lane receives them.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return lane_value(wave_inclusive_sum(v), kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const uint32_t r = row_max16_u32(v);
+  const uint32_t a = lane_value(r, 0), b = lane_value(r, 16), c = lane_value(r, 32),
+                 d = lane_value(r, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
 // Butterfly steps across 16-lane rows and 32-lane halves on the VALU (gfx950
 // v_permlane16_swap / v_permlane32_swap).  Swapping a value with itself
 // leaves, in every lane, the pair (x of the lane, x of the lane 16 -- resp. 32

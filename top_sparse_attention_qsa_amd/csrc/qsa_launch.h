@@ -42,6 +42,7 @@ struct SelectArgs {
   uint32_t* bitmap;          // global rows, may be null
   int32_t* token_ids;        // global rows, may be null
   int32_t* width;            // global rows, may be null
+  const float* widths = nullptr;  // certified rows: ChunkArgs::widths, local rows
 };
 
 struct GatherArgs {
@@ -138,6 +139,8 @@ struct ChunkArgs {
   float* bound;              // [rows][g_max] certified error bounds, may be null
   float* hi;                 // [rows][g_max] approx + bound, may be null
   uint32_t* lo_maxima;       // [rows][g_max/16] order keys of approx - bound, may be null
+  float* widths = nullptr;   // [rows][g_max/64] per 64-group tile, an upper bound of
+                             // hi - s over its groups (s: the chain score), may be null
 };
 
 // Exact rescoring inputs for the certified selection (chunk rows).

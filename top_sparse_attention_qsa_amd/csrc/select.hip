@@ -37,6 +37,8 @@ constexpr int kPerThread = 32;    // scores held per thread in one streaming pas
 struct alignas(16) SelectShared {
   uint32_t hist[3][256];  // radix passes rotate through three histograms
   uint32_t wave_tot[NWAVES];
+  uint32_t wave_aux[NWAVES];  // a second per-wavefront value (certified rows)
+  uint32_t counter;
   uint32_t cand_key[kCandCap];
   uint32_t cand_pos[kCandCap];
   uint32_t maxima[kMaxStage];
@@ -175,6 +177,7 @@ struct CertifiedScores {
   static constexpr bool kCertified = true;
   const float* q;    // this row's index query [HI][DI]
   const float* kp;   // this sequence's tiled pooled keys
+  const float* wrow; // this row's tile widths (chunk.hip), may be null
   __device__ uint32_t exact_key(uint32_t g) const {
     const float* kb = kp + (int64_t)(g >> 6) * (64 * DI) + (g & 63) * 4;
     float acc[HI];
@@ -207,7 +210,7 @@ struct CertifiedScores {
   // staged in `qs` (LDS scratch of DI * HI floats, dimension-major: entry
   // (d, i) holds heads i, 4+i, ...).  Called by the whole workgroup.
   __device__ void rescore_all(uint32_t* cand_key, const uint32_t* cand_pos, uint32_t n,
-                              float* qs) const {
+                              float* qs, const uint32_t* idx = nullptr) const {
     static_assert(HI % 4 == 0, "head quads");
     constexpr int HQ = HI / 4;
     constexpr int NC = DI / 4;
@@ -230,9 +233,12 @@ struct CertifiedScores {
     const int lane = lane_id();
     const int qi = lane & 3;
     for (uint32_t base = 64u * (uint32_t)wave_id(); base < n; base += 64u * NWAVES) {
-      const uint32_t c_i = base + (uint32_t)lane;
-      const bool valid = c_i < n;
-      const uint32_t g = cand_pos[valid ? c_i : 0u];  // n >= 1: lanes past n reread entry 0
+      const uint32_t j = base + (uint32_t)lane;
+      const bool valid = j < n;
+      // candidate j of the list (idx) or of the whole compaction; n >= 1, so
+      // lanes past n reread entry 0
+      const uint32_t c_i = idx ? idx[valid ? j : 0u] : (valid ? j : 0u);
+      const uint32_t g = cand_pos[c_i];
       const float* kb = kp + (int64_t)(g >> 6) * (64 * DI) + (g & 63) * 4;
       float4 ring[PF];
 #pragma unroll
@@ -272,6 +278,11 @@ struct FullKeys {
   const P* pol;
   __device__ uint32_t key(uint32_t i) const { return pol->full_key(i); }
 };
+
+// The float an order key came from (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 // Writes kept group g at output index o: token IDs 4g..4g+3 at 4o, and/or
 // bit g of the bitmap.
@@ -474,6 +485,15 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     uint32_t n_cand = 0;
     bool overflow = false;
     bool compacted = false;  // candidates already in LDS (segment-skipping pass)
+    // certified rows: this thread's share of the row's widest segment,
+    // loaded here so the loads overlap the threshold and compaction
+    float wpart = 0.0f;
+    if constexpr (P::kCertified) {
+      if (pol.wrow) {
+        const uint32_t tiles_w = (G + 63) / 64;
+        for (uint32_t t = tid; t < tiles_w; t += NT) wpart = fmaxf(wpart, pol.wrow[t]);
+      }
+    }
     uint32_t tau = 0, top = 0;  // with compacted: every candidate key is in [tau, top]
     const uint32_t segs = (G + kSegment - 1) / kSegment;
     if constexpr (!P::kCertified) {
@@ -581,11 +601,82 @@ __device__ void select_row(const P& pol, SelectShared& sh, const float* __restri
     }  // !compacted
     __syncthreads();
     if constexpr (P::kCertified) {
-      // the candidates' bounds are replaced by their exact (chain) keys; the
-      // query row is staged over the segment maxima, which are no longer read
+      // The candidates' keys are their upper bounds hi >= s (s: the chain
+      // score).  With W >= hi - s for every group of the row (the widest
+      // tile), fl(hi - W) <= s as well.  Let H_k and H_k1 be the k-th and
+      // (k+1)-th largest hi.  A candidate with hi < fl(H_k - W) is beaten by
+      // the k groups whose hi reaches H_k (their s >= fl(H_k - W)): it is
+      // out.  One with fl(hi - W) > H_k1 can be beaten only by groups whose
+      // hi exceeds H_k1, at most k of them counting itself: it is in.  Only
+      // the rest -- a band around the k-th score -- is rescored exactly, with
+      // the chain; "in" keys become the largest key, "out" keys 0 (below
+      // every score's key), and the exact selection below then picks the same
+      // set as the chain scores.  The query row is staged over the segment
+      // maxima, which are no longer read, and the band list after it.
       if (!overflow) {
-        static_assert(sizeof(SelectShared::maxima) >= sizeof(float) * 16 * 128, "query staging");
-        pol.rescore_all(sh.cand_key, sh.cand_pos, n_cand, reinterpret_cast<float*>(sh.maxima));
+        static_assert(sizeof(SelectShared::maxima) >= sizeof(float) * 16 * 128 * 2,
+                      "query staging and band list");
+        float* qs = reinterpret_cast<float*>(sh.maxima);
+        uint32_t* band = sh.maxima + 16 * 128;
+        constexpr uint32_t kBandCap = kMaxStage - 16 * 128;
+        bool all = pol.wrow == nullptr || n_cand <= (uint32_t)k;
+        if (!all) {
+          const int lane = lane_id(), wave = wave_id();
+          // W: the row's widest tile
+          const float ww = wave_max(wpart);
+          if (lane == 0) sh.wave_aux[wave] = __float_as_uint(ww);
+          if (tid == 0) sh.counter = 0u;
+          uint32_t T1, above1;
+          radix_kth_largest(LdsCands{sh.cand_key}, n_cand, (uint32_t)k, sh, &T1, &above1);
+          float W = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w) W = fmaxf(W, __uint_as_float(sh.wave_aux[w]));
+          // keys equal to H_k, and the largest key below it
+          uint32_t eq = 0u, below = 0u;
+          for (uint32_t i = tid; i < n_cand; i += NT) {
+            const uint32_t key = sh.cand_key[i];
+            eq += key == T1 ? 1u : 0u;
+            below = (key < T1 && key > below) ? key : below;
+          }
+          const uint32_t eq_w = (uint32_t)wave_sum_u32(eq);
+          const uint32_t below_w = wave_max_u32(below);
+          __syncthreads();  // every wavefront has read wave_aux (W)
+          if (lane == 0) {
+            sh.wave_tot[wave] = eq_w;
+            sh.wave_aux[wave] = below_w;
+          }
+          __syncthreads();
+          uint32_t eq_all = 0u, below_all = 0u;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w) {
+            eq_all += sh.wave_tot[w];
+            below_all = sh.wave_aux[w] > below_all ? sh.wave_aux[w] : below_all;
+          }
+          const float hk = key_value(T1);
+          const uint32_t T2 = above1 + eq_all > (uint32_t)k ? T1 : below_all;
+          const float hk1 = T2 == 0u ? -INFINITY : key_value(T2);
+          const float out_below = hk - W;
+          for (uint32_t i = tid; i < n_cand; i += NT) {
+            const float h = key_value(sh.cand_key[i]);
+            if (h < out_below) {
+              sh.cand_key[i] = 0u;
+            } else if (h - W > hk1) {
+              sh.cand_key[i] = 0xFFFFFFFFu;
+            } else {
+              const uint32_t slot = atomicAdd(&sh.counter, 1u);
+              if (slot < kBandCap) band[slot] = i;
+            }
+          }
+          __syncthreads();
+          const uint32_t n_band = sh.counter;
+          if (n_band <= kBandCap) {
+            if (n_band > 0) pol.rescore_all(sh.cand_key, sh.cand_pos, n_band, qs, band);
+          } else {
+            all = true;  // a wide band: every candidate is rescored
+          }
+          __syncthreads();  // the counter and the band list are read above
+        }
+        if (all) pol.rescore_all(sh.cand_key, sh.cand_pos, n_cand, qs);
         __syncthreads();
       }
     }
@@ -685,13 +776,15 @@ select_certified_kernel(const float* __restrict__ scores, const uint32_t* __rest
                         int32_t k, int64_t row0, uint32_t* __restrict__ bitmap,
                         int32_t* __restrict__ token_ids, int32_t* __restrict__ width,
                         const float* __restrict__ index_q, const float* __restrict__ pooled,
-                        const int64_t* __restrict__ pooled_off) {
+                        const int64_t* __restrict__ pooled_off,
+                        const float* __restrict__ widths) {
   __shared__ SelectShared sh;
   const int64_t lrow = blockIdx.x;
   const int64_t row = row0 + lrow;
   const RowView rv = row_view(seq_len, row, queries, g_max);
   const CertifiedScores<HI, DI> pol{index_q + row * (int64_t)(HI * DI),
-                                    pooled + (rv.valid ? pooled_off[rv.b] : 0)};
+                                    pooled + (rv.valid ? pooled_off[rv.b] : 0),
+                                    widths ? widths + lrow * (g_max / 64) : nullptr};
   select_row(pol, sh, scores, maxima, rv, lrow, row, g_max, k, bitmap, token_ids, width);
 }
 
@@ -798,7 +891,7 @@ template <int HI, int DI>
 hipError_t launch_cert_t(const SelectArgs& a, const RescoreArgs& r, hipStream_t s) {
   hipLaunchKernelGGL((select_certified_kernel<HI, DI>), dim3((unsigned)a.rows), dim3(NT), 0, s,
                      a.scores, a.maxima, a.seq_len, a.queries, a.g_max, a.k, a.row0, a.bitmap,
-                     a.token_ids, a.width, r.index_q, r.pooled, r.pooled_off);
+                     a.token_ids, a.width, r.index_q, r.pooled, r.pooled_off, a.widths);
   return hipGetLastError();
 }
 
