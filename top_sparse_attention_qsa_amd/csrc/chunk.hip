@@ -64,6 +64,19 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   const int64_t grow0 = row0 + lrow0;
   const int b = (int)(grow0 / queries);            // all RB rows share this sequence
 
+  // the longest row of the workgroup sets the tile range; shorter rows mask.
+  // A workgroup whose four tiles all lie past it leaves before staging
+  // anything (with rows of very different lengths, most of the grid).
+  int64_t g_rows[RB];
+  int64_t g_max_rows = 0;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const RowView rv = row_view(seq_len, grow0 + r, queries, g_max);
+    g_rows[r] = rv.valid ? rv.g : -1;
+    g_max_rows = rv.g > g_max_rows && rv.valid ? rv.g : g_max_rows;
+  }
+  if ((int64_t)blockIdx.y * 4 * 64 >= g_max_rows) return;
+
   // stage A fragments: A[i][kk] of M-tile m, k-step 4q + s = q[row][head][16q + 4kk + s]
   // with M-row i -> (row m*RPM + i/HI, head i%HI), i = lane%16, kk = lane/16.
   // Each thread moves NQ float4s (four consecutive dimensions each), all
@@ -105,15 +118,6 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   }
   __syncthreads();
 
-  // the longest row of the workgroup sets the tile range; shorter rows mask
-  int64_t g_rows[RB];
-  int64_t g_max_rows = 0;
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const RowView rv = row_view(seq_len, grow0 + r, queries, g_max);
-    g_rows[r] = rv.valid ? rv.g : -1;
-    g_max_rows = rv.g > g_max_rows && rv.valid ? rv.g : g_max_rows;
-  }
   const int64_t tile = (int64_t)blockIdx.y * 4 + wave;
   if (tile * 64 >= g_max_rows) return;
 
