@@ -15,11 +15,13 @@
 // rounding-error bound of an n-term sum, once for the MFMA order, allowing an
 // extra rounding per product, and once for the chain; sum_d |q_d k_d| is
 // bounded by Cauchy-Schwarz; ReLU is 1-Lipschitz; the final 2 absorbs the
-// rounding of E itself).  The kernel writes hi = s~ + E as the row's score and
-// the per-16-group maxima of the order key of lo = s~ - E.  The selection
-// kernel then keeps every group whose hi reaches a lower bound of the k-th
-// largest lo, rescores those exactly with the chain, and selects among them,
-// so the chosen set equals the one the chain scores give (see select.hip).
+// rounding of E itself).  The kernel writes hi = s~ + E as the row's score,
+// the per-16-group maxima of the order key of lo = s~ - E, and per 64-group
+// tile a width W >= hi - s.  The selection kernel keeps every group whose hi
+// reaches a lower bound of the k-th largest lo, settles by their bounds which
+// of those are certainly in or out, rescores the rest exactly with the chain
+// and selects among them, so the chosen set equals the one the chain scores
+// give (see select.hip).
 //
 // Mapping: a workgroup owns 4 M-tiles of 16 (row, head) pairs (16/H_I rows
 // each) and 4 wavefronts; each wavefront owns one 64-group pooled-key tile

@@ -21,6 +21,9 @@
 //  4. An ordered pass keeps every key above T and the first (k - above)
 //     keys equal to T in position order -- the tie rule -- and writes each
 //     kept group at its output index, which is already chronological.
+// Causal-chunk rows (select_certified_kernel) hold upper bounds of the chain
+// scores instead; between steps 2 and 3 their candidates are settled by
+// bounds where possible and the rest rescored exactly (CertifiedScores).
 // No sort, no float atomics; the result is unique, so it is bit-identical to
 // any correct selector.
 #include "qsa_internal.h"
