@@ -53,12 +53,12 @@ def algorithmic_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=128, k=5
 def implementation_overhead_bytes(B=32, G=65536, h_q=32, d=128, k=512):
     """Traffic of this implementation beyond the method's bytes: the per-16-
     group score maxima (written by the scoring kernel, read by the selection)
-    and the attention's chunk partials (written per 64-row chunk, read by the
-    merge).  The decode path writes no selection bitmap (the selection writes
-    token IDs directly), so the bitmap entries of the method's table are not
-    moved either."""
-    chunks = math.ceil((4 * k + 3) / 64)
-    return dict(maxima=2 * B * (G // 16) * 4, attention_partials=2 * B * h_q * chunks * (d + 2) * 4,
+    and the attention's range partials (one per 8 consecutive 64-row chunks,
+    written by the attention, read by the merge).  The decode path writes no
+    selection bitmap (the selection writes token IDs directly), so the bitmap
+    entries of the method's table are not moved either."""
+    parts = math.ceil(math.ceil((4 * k + 3) / 64) / 8)
+    return dict(maxima=2 * B * (G // 16) * 4, attention_partials=2 * B * h_q * parts * (d + 2) * 4,
                 bitmap_not_moved=-2 * B * G // 8)
 
 
@@ -68,8 +68,8 @@ def stage_bytes(B=32, G=65536, h_i=16, d_i=128, h_q=32, h_kv=4, d=128, k=512):
     W = 4 * k
     kv_row = h_kv * d * 4
     seg = G // 16
-    chunks = math.ceil((4 * k + 3) / 64)
-    part = B * h_q * chunks * (d + 2) * 4
+    parts = math.ceil(math.ceil((4 * k + 3) / 64) / 8)  # range partials per (row, head)
+    part = B * h_q * parts * (d + 2) * 4
     return dict(
         score=B * G * d_i * 4 + B * h_i * d_i * 4 + B * G * 4 + B * seg * 4,
         select_emit=B * G * 4 + B * seg * 4 + B * (W + 4) * 4 + B * 4,

@@ -59,7 +59,7 @@ extern "C" {
 #define QSA_KEY_TILE 64      /* groups per pooled-key tile (layout below)          */
 #define QSA_DECODE_STAGES 5  /* stages timed by qsa_timer in one qsa_decode call:
                                 score, select+emit, resolve+gather, attention
-                                chunks, merge of the chunk partials               */
+                                chunks, merge of the range partials               */
 
 typedef void *qsa_stream; /* a hipStream_t */
 
@@ -213,8 +213,10 @@ QSA_API int qsa_resolve_gather(const qsa_shape *shape, const int32_t *token_ids,
  * row, out = softmax(scale * q . k) . v per query head ([SET] §Floating
  * point makes order observable; [MASK] §Decision).  Rows are visited in
  * chronological order in fixed chunks of consecutive rows whose partial
- * (max, denominator, accumulator) states are merged in ascending chunk
- * order, so results are run-to-run bit-identical.  width 0 gives out = +0
+ * (max, denominator, accumulator) states are folded in ascending chunk
+ * order (one state per range of consecutive chunks, the range states then
+ * merged in ascending order), so results depend on the width alone and are
+ * run-to-run bit-identical.  width 0 gives out = +0
  * and lse = -inf.  lse may be NULL. */
 QSA_API int qsa_online_attend(const qsa_shape *shape, const float *q, const float *k_compact,
                       const float *v_compact, const int32_t *width, float softmax_scale,

@@ -142,7 +142,8 @@ std::vector<Region> expected_regions(const qsa_shape& s) {
   const int64_t rows = (int64_t)s.batch * s.queries;
   const int64_t R = (s.rows_in_flight > 0 && s.rows_in_flight < rows) ? s.rows_in_flight : rows;
   const int64_t stride = 4 * (int64_t)s.budget_groups + 4;
-  const int64_t chunks = (4 * (int64_t)s.budget_groups + 3 + 63) / 64;
+  // attention partials: one per 8 consecutive chunks of 64 compact rows
+  const int64_t chunks = ((4 * (int64_t)s.budget_groups + 3 + 63) / 64 + 7) / 8;
   std::vector<Region> r;
   r.push_back({"scores", 0, (uintptr_t)(R * s.max_groups * 4)});
   r.push_back({"maxima", 0, (uintptr_t)(R * (s.max_groups / 16) * 4)});

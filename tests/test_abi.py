@@ -63,7 +63,7 @@ def test_workspace_scales_with_groups_and_width_never_tokens():
     # (4 B / 64 groups) + compact K/V + partials
     per_row_compact = 2 * (4 * 512 + 4) * 4 * 128 * 4
     per_row_groups = 65536 * 4 + 65536 // 16 * 4 + 65536 // 64 * 4
-    per_row_part = 32 * 33 * (128 + 2) * 4
+    per_row_part = 32 * 5 * (128 + 2) * 4  # 33 chunks of 64 rows, one partial per 8
     # union gather: row bitmap, union bitmap and word prefixes (at most one
     # sequence per row), union list, position list
     per_row_union = 3 * (65536 // 32 + 1) * 4 + 513 * 8 + (4 * 512 + 4) * 4

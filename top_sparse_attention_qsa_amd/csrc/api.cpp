@@ -91,7 +91,7 @@ Layout layout(const qsa_shape* s) {
   off = align256(off + compact);
   L.vc = off;
   off = align256(off + compact);
-  const size_t slots = (size_t)R * s->q_heads * attn_chunks(s);
+  const size_t slots = (size_t)R * s->q_heads * attn_parts(attn_chunks(s));
   L.pacc = off;
   off = align256(off + slots * s->head_dim * sizeof(float));
   L.pml = off;

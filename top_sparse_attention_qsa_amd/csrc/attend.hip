@@ -7,11 +7,16 @@
 // the width alone: the compact row is cut into chunks of kAttnChunk
 // consecutive rows; each chunk produces a partial (max m_c, denominator l_c,
 // accumulator acc_c) with a fixed butterfly for the denominator and a
-// chronological accumulation over the chunk's rows; the partials are merged
-// in ascending chunk order (running maximum, rescale, denominator and
-// accumulator updates).  No float atomics: results are run-to-run identical.
+// chronological accumulation over the chunk's rows; the partials of each
+// range of kAttnRange consecutive chunks are folded in ascending chunk order
+// into one range partial (running maximum, rescale, denominator and
+// accumulator updates), and the range partials are merged the same way in
+// ascending range order.  No float atomics: results are run-to-run identical.
 //
-// attend_chunk_kernel: one workgroup per (chunk, KV head, row) serves every
+// attend_chunk_kernel: a persistent workgroup walks its (range, KV head, row)
+// items chunk by chunk, keeping the range's running partial in registers and
+// storing it after the range's last chunk, so the merge reads one partial
+// per range instead of one per chunk.  Each chunk serves every
 // query head of the KV head's GQA group (query head hq reads KV head
 // hq / (H_q/H_kv)).  Scores: the chunk's K rows and query heads are staged
 // in LDS; wavefront w scores rows 16w..16w+15 for every head of the group on
@@ -32,6 +37,7 @@ namespace qsa {
 namespace {
 
 constexpr int C = kAttnChunk;
+constexpr int RC = kAttnRange;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -60,9 +66,11 @@ struct AttnCfg {
   static constexpr int SFLOATS = KFLOATS > RFLOATS ? KFLOATS : RFLOATS;
 };
 
-// Work item it -> (chunk, local row, KV head), chunk-major, so that the items
-// of one chunk index are consecutive and a launch whose grid divides the item
-// count of the non-empty chunks gives every workgroup the same amount of work.
+// Work item it -> (range, local row, KV head), range-major, so that the items
+// of one range index are consecutive and a launch whose grid divides the item
+// count of the non-empty ranges gives every workgroup the same amount of
+// work.  The `chunk` digit of an item holds its range; a position inside the
+// item adds the chunk's offset in the range.
 struct Item {
   int chunk;
   int hk;
@@ -79,9 +87,9 @@ __device__ __forceinline__ Item item_of(int64_t it, int64_t rows, int kv_heads) 
 }
 
 // Stepping a workgroup's item by the grid size adds the grid size's own
-// (chunk, row, head) digits with carries, so the item loop does no 64-bit
+// (range, row, head) digits with carries, so the item loop does no 64-bit
 // division (which the compiler expands to over a hundred scalar
-// instructions).  Digits past the last chunk are only used behind `it < items`.
+// instructions).  Digits past the last range are only used behind `it < items`.
 __device__ __forceinline__ Item item_step(Item x, const Item& step, int64_t rows, int kv_heads) {
   x.hk += step.hk;
   int64_t carry = 0;
@@ -148,7 +156,11 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   const int tid = (int)threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
-  const int64_t items = (int64_t)n_chunks * rows * kv_heads;
+  // range items (range of RC consecutive chunks, local row, KV head),
+  // range-major; a workgroup walks the chunks of each of its range items in
+  // order and folds their partials into one per range
+  const int n_ranges = attn_parts(n_chunks);
+  const int64_t items = (int64_t)n_ranges * rows * kv_heads;
   const int64_t rstride = (int64_t)kv_heads * D;  // floats between compact or cache rows
 
   // Every load is unconditional: rows past a chunk's width read zeros (compact
@@ -305,28 +317,46 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     }
   };
 
-  int64_t it = blockIdx.x;
-  int j = 0;  // this workgroup's item sequence number
-  // raw digits of items it, it+grid, it+2*grid; past the end, the last item
-  // (whose rows always exist) stands in for address computations
+  // positions: range item `it` (digits r: range, row, head) and chunk `sub`
+  // of the range; past the last range item, the last range item's first
+  // chunk stands in for address computations
+  struct Pos {
+    int64_t it;
+    Item r;
+    int sub;
+  };
   const Item step = item_of(gridDim.x, rows, kv_heads);
   const Item last = item_of(items - 1, rows, kv_heads);
-  Item raw0 = item_of(it, rows, kv_heads);
-  Item raw1 = item_step(raw0, step, rows, kv_heads);
-  Item raw2 = item_step(raw1, step, rows, kv_heads);
-  auto item_at = [&](int64_t i, const Item& raw) { return i < items ? raw : last; };
-  auto rows_at = [&](int64_t i, const Item& x) { return i < items ? chunk_rows(x) : 0; };
-  Item cur = item_at(it, raw0);
-  int cn = rows_at(it, cur);
+  auto chunk_of = [&](const Pos& p) -> Item {
+    Item x = p.it < items ? p.r : last;
+    x.chunk = x.chunk * RC + (p.it < items ? p.sub : 0);
+    return x;
+  };
+  auto rows_of = [&](const Pos& p) -> int { return p.it < items ? chunk_rows(chunk_of(p)) : 0; };
+  // the next position: the next chunk of the range while it has rows, else
+  // the first chunk of the workgroup's next range item
+  auto advance = [&](const Pos& p) -> Pos {
+    if (p.it < items && p.sub + 1 < RC) {
+      Pos q = p;
+      ++q.sub;
+      if (rows_of(q) > 0) return q;
+    }
+    return Pos{p.it + (int64_t)gridDim.x, item_step(p.r, step, rows, kv_heads), 0};
+  };
+  int j = 0;  // this workgroup's chunk sequence number
+  Pos pcur{(int64_t)blockIdx.x, item_of(blockIdx.x, rows, kv_heads), 0};
+  Item cur = chunk_of(pcur);
+  int cn = rows_of(pcur);
   if constexpr (FUSED) {
-    // items 0 and 1 of this workgroup are resolved up front
-    const Item x1 = item_at(it + gridDim.x, raw1);
+    // chunks 0 and 1 of this workgroup are resolved up front
+    const Pos p1 = advance(pcur);
+    const Item x1 = chunk_of(p1);
     resolve_ids(cur, cn);
     resolve_slots(cur, cn);
     resolve_store(0, cn);
-    resolve_ids(x1, rows_at(it + gridDim.x, x1));
-    resolve_slots(x1, rows_at(it + gridDim.x, x1));
-    resolve_store(1, rows_at(it + gridDim.x, x1));
+    resolve_ids(x1, rows_of(p1));
+    resolve_slots(x1, rows_of(p1));
+    resolve_store(1, rows_of(p1));
     __syncthreads();
   }
   // K, then q, then V here as in the loop: the wait for K and q at the top of
@@ -337,21 +367,24 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   load_q(cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, cn, 0);
-  while (it < items) {
-    const int64_t it_next = it + gridDim.x;
-    const int64_t it_next2 = it_next + gridDim.x;
-    const Item nxt = item_at(it_next, raw1);
-    const int cn_next = rows_at(it_next, nxt);
-    const Item nxt2 = item_at(it_next2, raw2);
-    const int cn_next2 = rows_at(it_next2, nxt2);
+  // the range's running partial for this thread's outputs
+  float4 racc[OV4];
+  float rm[OV4], rl[OV4];
+#pragma unroll
+  for (int r = 0; r < OV4; ++r) {
+    racc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rm[r] = -INFINITY;
+    rl[r] = 0.0f;
+  }
+  while (pcur.it < items) {
+    const Pos pnx = advance(pcur);
+    const Pos pnx2 = advance(pnx);
+    const Item nxt = chunk_of(pnx);
+    const int cn_next = rows_of(pnx);
+    const Item nxt2 = chunk_of(pnx2);
+    const int cn_next2 = rows_of(pnx2);
     const int rs_cur = FUSED ? j % 3 : 0, rs_next = FUSED ? (j + 1) % 3 : 0;
-    // A workgroup whose last item has no rows stops here (chunk-major items
-    // put the empty chunks of rows shorter than the longest possible width
-    // last, so this is the common case; the loads prefetched for the item are
-    // discarded).  Any other item with no rows runs the same code on masked
-    // rows and skips its stores, so every prefetch is issued from one program
-    // point.
-    if (cn == 0 && it_next >= items) break;
+    if (cn == 0 && pnx.it >= items) break;
     {
       // stage this item's K in LDS (rows past the width hold a copy of the
       // last row -- their scores are replaced by -inf, so they are never
@@ -479,18 +512,11 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 #pragma unroll
         for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
       __syncthreads();
-      const int64_t slot0 = (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_chunks + cur.chunk;
-      if (tid < GQ && cn > 0) {
-        float m = mw_sh[0][tid];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) m = fmaxf(m, mw_sh[w][tid]);
-        const float l = (lw_sh[0][tid] + lw_sh[1][tid]) + (lw_sh[2][tid] + lw_sh[3][tid]);
-        *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)tid * n_chunks) * 2) =
-            make_float2(m, l);
-      }
-      // four consecutive outputs per thread and a fixed store count per item
-      // (a store loop of runtime length made the compiler wait for every
-      // outstanding load, the next item's V included, at the top of the item)
+      // fold this chunk's partial into the range's (online rescale: running
+      // maximum, weights exp(m - m')), and store it after the range's last chunk
+      const int64_t slot0 =
+          (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_ranges + cur.chunk / RC;
+      const bool range_end = pnx.sub == 0;
       if (cn > 0) {
 #pragma unroll
         for (int r = 0; r < OV4; ++r) {
@@ -507,29 +533,52 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
               sum.z = sum.z + t.z;
               sum.w = sum.w + t.w;
             }
-            *reinterpret_cast<float4*>(part_acc + (slot0 + (int64_t)h * n_chunks) * D + d) = sum;
+            float mc = mw_sh[0][h];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mc = fmaxf(mc, mw_sh[w][h]);
+            const float lc = (lw_sh[0][h] + lw_sh[1][h]) + (lw_sh[2][h] + lw_sh[3][h]);
+            if (pcur.sub == 0) {
+              racc[r] = sum;
+              rm[r] = mc;
+              rl[r] = lc;
+            } else {
+              const float mn = fmaxf(rm[r], mc);
+              const float a = expf(rm[r] - mn), b = expf(mc - mn);
+              racc[r].x = racc[r].x * a + sum.x * b;
+              racc[r].y = racc[r].y * a + sum.y * b;
+              racc[r].z = racc[r].z * a + sum.z * b;
+              racc[r].w = racc[r].w * a + sum.w * b;
+              rl[r] = rl[r] * a + lc * b;
+              rm[r] = mn;
+            }
+            if (range_end) {
+              *reinterpret_cast<float4*>(part_acc + (slot0 + (int64_t)h * n_ranges) * D + d) =
+                  racc[r];
+              if (d == 0)
+                *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)h * n_ranges) * 2) =
+                    make_float2(rm[r], rl[r]);
+            }
           }
         }
       }
       resolve_store(FUSED ? (j + 2) % 3 : 0, cn_next2);  // visible after the next item's first barrier
     }
-    it = it_next;
-    raw1 = raw2;
-    raw2 = item_step(raw2, step, rows, kv_heads);
+    pcur = pnx;
     cur = nxt;
     cn = cn_next;
     ++j;
   }
 }
 
-// Merge of the chunk partials of one (query head, row): lane c holds chunk
+// Merge of the range partials of one (query head, row): lane c holds range
 // c's (m_c, l_c) and its weight a_c = exp(m_c - m); four wavefronts each fold
-// a contiguous quarter of the chunks in ascending order (weights broadcast
+// a contiguous quarter of the ranges in ascending order (weights broadcast
 // from their lanes), then the quarters are added in order.  Every load a
 // wavefront needs -- all (m_c, l_c) and its quarter's accumulators -- is
 // issued before the first use, so the merge costs one memory round trip.
 constexpr int kMaxChunks = (4 * QSA_MAX_BUDGET + 3 + C - 1) / C;  // 65
-constexpr int kMaxQuarter = (kMaxChunks + 3) / 4;                  // 17
+constexpr int kMaxParts = attn_parts(kMaxChunks);                  // 9
+constexpr int kMaxQuarter = (kMaxParts + 3) / 4;                   // 3
 
 template <int D>
 __global__ void __launch_bounds__(4 * kWave)
@@ -537,7 +586,7 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
              const int32_t* __restrict__ width, int32_t q_heads, int32_t n_chunks,
              int32_t stride, int64_t row0, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int DPL = D / kWave;
-  static_assert(kMaxChunks <= 2 * kWave, "two chunk batches per lane at most");
+  static_assert(kMaxParts <= kWave, "one range partial per lane at most");
   __shared__ float red[4][D + 1];
   const int wave = wave_id();
   const int lane = lane_id();
@@ -555,19 +604,16 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
     }
     return;
   }
-  const int nc = (w + C - 1) / C;
-  const int64_t base = (lrow * q_heads + hq) * n_chunks;
+  const int nc = attn_parts((w + C - 1) / C);  // range partials of this row
+  const int64_t base = (lrow * q_heads + hq) * attn_parts(n_chunks);
   const int per = (nc + 3) / 4;
   const int cb = wave * per;
   const int cnt = (cb + per) < nc ? per : (nc > cb ? nc - cb : 0);
-  // loads: (m, l) of chunks lane and lane + 64; this quarter's accumulators
-  // (indexes are clamped to chunk nc-1, so every load is in bounds)
+  // loads: (m, l) of range lane; this quarter's accumulators (indexes are
+  // clamped to range nc-1, so every load is in bounds)
   const int c0 = lane < nc ? lane : nc - 1;
-  const int c1 = lane + kWave < nc ? lane + kWave : nc - 1;
   float2 ml0 = *reinterpret_cast<const float2*>(part_ml + (base + c0) * 2);
-  float2 ml1 = *reinterpret_cast<const float2*>(part_ml + (base + c1) * 2);
   if (lane >= nc) ml0 = make_float2(-INFINITY, 0.0f);
-  if (lane + kWave >= nc) ml1 = make_float2(-INFINITY, 0.0f);
   float pa[kMaxQuarter][DPL];
 #pragma unroll
   for (int t = 0; t < kMaxQuarter; ++t) {
@@ -575,11 +621,9 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
 #pragma unroll
     for (int j = 0; j < DPL; ++j) pa[t][j] = part_acc[(base + c) * D + lane * DPL + j];
   }
-  const float m = wave_max(fmaxf(ml0.x, ml1.x));
-  // weights: lane holds chunk lane (a0) and chunk lane + 64 (a1)
+  const float m = wave_max(ml0.x);
   const float a0 = lane < nc ? expf(ml0.x - m) : 0.0f;
-  const float a1 = lane + kWave < nc ? expf(ml1.x - m) : 0.0f;
-  const float wl0 = ml0.y * a0, wl1 = ml1.y * a1;
+  const float wl0 = ml0.y * a0;
   float l = 0.0f;
   float acc[DPL];
 #pragma unroll
@@ -588,8 +632,8 @@ merge_kernel(const float* __restrict__ part_acc, const float* __restrict__ part_
   for (int t = 0; t < kMaxQuarter; ++t) {
     if (t < cnt) {  // uniform
       const int c = cb + t;
-      const float a = c < kWave ? read_lane(a0, c) : read_lane(a1, c - kWave);
-      l = l + (c < kWave ? read_lane(wl0, c) : read_lane(wl1, c - kWave));
+      const float a = read_lane(a0, c);
+      l = l + read_lane(wl0, c);
 #pragma unroll
       for (int j = 0; j < DPL; ++j) acc[j] = __builtin_fmaf(pa[t][j], a, acc[j]);
     }
@@ -639,7 +683,7 @@ hipError_t launch_attend_t(const AttendArgs& a, hipStream_t s) {
     per_cu = n;
     per_cu_cache.store(n, std::memory_order_relaxed);
   }
-  const int64_t items = (int64_t)a.n_chunks * a.rows * a.kv_heads;
+  const int64_t items = (int64_t)attn_parts(a.n_chunks) * a.rows * a.kv_heads;
   const int64_t slots = (int64_t)device_cus() * per_cu;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
   RowSource src{a.k_compact, a.v_compact, MODE == kUnion ? a.union_pos : a.token_ids, a.seq_len,

@@ -14,7 +14,8 @@
 namespace qsa {
 
 constexpr int kSegment = 16;          // groups per maximum used to bound the threshold
-constexpr int kAttnChunk = 64;        // compact rows per attention partial
+constexpr int kAttnChunk = 64;        // compact rows per attention chunk
+constexpr int kAttnRange = 8;         // consecutive chunks folded into one partial
 constexpr int kUnionScanWords = 4096; // union bitmap words per count/list block
 
 struct ScoreArgs {
@@ -78,8 +79,8 @@ struct AttendArgs {
   float scale;
   int64_t row0;
   int64_t rows;
-  float* part_acc;           // [rows][H_q][n_chunks][D] local rows
-  float* part_ml;            // [rows][H_q][n_chunks][2]
+  float* part_acc;           // [rows][H_q][attn_parts(n_chunks)][D] local rows
+  float* part_ml;            // [rows][H_q][attn_parts(n_chunks)][2]
   float* out;                // global rows
   float* lse;                // global rows, may be null
   // fused path (token_ids != null): rows are read from the cache through the
@@ -180,6 +181,12 @@ int launch_dense_ids(const int32_t* seq_len, int32_t queries, int32_t k, int64_t
 int launch_chunk(const ChunkArgs& a, int h_i, int d_i, void* stream);
 int launch_select_certified(const SelectArgs& a, const RescoreArgs& r, void* stream);
 int launch_union(const UnionArgs& a, void* stream);
+
+// Attention partials per row and query head for n_chunks chunks: one per
+// range of kAttnRange consecutive chunks.
+inline constexpr int attn_parts(int n_chunks) {
+  return (n_chunks + kAttnRange - 1) / kAttnRange;
+}
 
 // Compute units of the current device (256 if it cannot be queried).
 int device_cus();
