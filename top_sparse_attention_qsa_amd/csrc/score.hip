@@ -9,7 +9,8 @@
 //
 // Mapping: one lane owns one group and a wavefront owns one pooled-key tile of
 // 64 groups; in the tiled layout, dimension chunk c of a tile is 1 KiB
-// contiguous, so each float4 load of the wave is one coalesced 1 KiB read.
+// contiguous, so each float4 load of the wave is one coalesced 1 KiB read,
+// issued a few chunks ahead of its use.
 // With 4, 8 or 16 index heads the multiply-adds run on the matrix cores
 // (score_mfma_kernel: v_mfma_f32_4x4x1_16b_f32 rounds each step once, like
 // fmaf, so the bits are those of the chain); the query row is staged in LDS.
@@ -72,6 +73,18 @@ __device__ __forceinline__ void store_scores(float* __restrict__ srow, uint32_t*
   }
 }
 
+// Residency and load depth of score_mfma_kernel.  Four workgroups (16
+// wavefronts) per compute unit, each wavefront with four 1 KiB chunk loads in
+// flight, read the pooled keys faster than the eight workgroups with two
+// chunks in flight that fit by registers (163.9 against 168.5 us over the
+// decode batch's 1 GiB; five per compute unit did as well as four, six,
+// eight-chunk rings or eight tiles per wavefront did worse).  The cap is set
+// by reserving LDS at launch: a quarter of the compute unit's 160 KiB per
+// workgroup.
+constexpr int kScoreMfmaRing = 4;
+constexpr int kScoreWgsPerCu = 4;
+constexpr int kLdsPerCu = 160 * 1024;
+
 // Matrix-core form of score_kernel for HI a multiple of 4: the same lanes,
 // loads and fused multiply-adds in the same order, issued as
 // v_mfma_f32_4x4x1_16b_f32.  With one product per step, block b of that
@@ -104,7 +117,7 @@ score_mfma_kernel(const float* __restrict__ index_q, const float* __restrict__ p
   const TileLoader ld{buffer_over(tbase, 64 * DI * 4)};
 
   constexpr int NC = DI / 4;
-  constexpr int PF = 2;  // the same ring as score_kernel
+  constexpr int PF = kScoreMfmaRing;
   static_assert(NC % PF == 0, "ring depth must divide the chunk count");
   float4 ring[PF];
   if (active) {
@@ -276,10 +289,16 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int64_t tiles = (a.g_max + 63) / 64;
   dim3 grid((unsigned)((tiles + kScoreWaves - 1) / kScoreWaves), (unsigned)a.rows);
   if (grid.x == 0 || a.rows == 0) return hipSuccess;
-  if constexpr (HI % 4 == 0)
-    hipLaunchKernelGGL((score_mfma_kernel<HI, DI>), grid,
-                       dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
-                       a.seq_len, a.queries, a.g_max, a.row0, a.scores, a.maxima);
+  if constexpr (HI % 4 == 0) {
+    // the query staging (qs) is the kernel's only LDS; the rest of the
+    // workgroup's share is reserved to cap residency
+    constexpr int staged = DI * HI * 4;
+    constexpr int reserve = kLdsPerCu / kScoreWgsPerCu - staged;
+    static_assert(reserve >= 0, "query staging exceeds the workgroup's LDS share");
+    hipLaunchKernelGGL((score_mfma_kernel<HI, DI>), grid, dim3(kScoreWaves * kWave), reserve, s,
+                       a.index_q, a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0,
+                       a.scores, a.maxima);
+  }
   else
     hipLaunchKernelGGL((score_kernel<HI, DI>), grid,
                        dim3(kScoreWaves * kWave), 0, s, a.index_q, a.pooled, a.pooled_off,
