@@ -53,12 +53,17 @@ pool_kernel(const float* __restrict__ raw, const int64_t* __restrict__ raw_off,
   *reinterpret_cast<float4*>(dst) = s;
 }
 
+constexpr int kPoolWgsPerCu = 4;
+
 template <int DI>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
   const int64_t elems = a.g_max * (DI / 4);
   dim3 grid((unsigned)((elems + 255) / 256), (unsigned)a.batch);
   if (grid.x == 0 || a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel<DI>, grid, dim3(256), 0, s, a.raw_keys, a.raw_off, a.seq_len,
+  // four workgroups per compute unit: 0.941 ms against 0.982 ms for the eight
+  // that fit by threads (4 GiB read, 1 GiB written; three to five per compute
+  // unit did about as well, six or more no better than eight)
+  hipLaunchKernelGGL(pool_kernel<DI>, grid, dim3(256), lds_reserve(kPoolWgsPerCu, 0), s, a.raw_keys, a.raw_off, a.seq_len,
                      a.first_group, a.pooled, a.pooled_off, a.g_max);
   return hipGetLastError();
 }

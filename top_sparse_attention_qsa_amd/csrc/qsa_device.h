@@ -15,6 +15,16 @@ constexpr int kSelectThreads = 1024;  // one selection workgroup per row
 constexpr int kCandCap = 4096;        // candidates kept in LDS before the streaming path
 constexpr int kGatherTokens = 8;      // compact rows per gather workgroup
 
+// Residency caps for the streaming kernels.  With fewer wavefronts per SIMD
+// than registers would admit, the pooled-key sweep and the pooling read HBM
+// faster (measured on this part); a launch caps residency by reserving LDS,
+// a 1/wgs_per_cu share of the compute unit's 160 KiB per workgroup, less
+// what the kernel declares itself.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int lds_reserve(int wgs_per_cu, int static_bytes) {
+  return kLdsPerCu / wgs_per_cu - static_bytes;
+}
+
 // Scores are ordered through a monotone unsigned key: -0 is folded onto +0,
 // then non-negative floats get their sign bit set and negative floats are
 // bit-inverted, so unsigned comparison equals float comparison.

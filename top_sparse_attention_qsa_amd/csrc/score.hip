@@ -79,11 +79,9 @@ __device__ __forceinline__ void store_scores(float* __restrict__ srow, uint32_t*
 // chunks in flight that fit by registers (163.9 against 168.5 us over the
 // decode batch's 1 GiB; five per compute unit did as well as four, six,
 // eight-chunk rings or eight tiles per wavefront did worse).  The cap is set
-// by reserving LDS at launch: a quarter of the compute unit's 160 KiB per
-// workgroup.
+// by reserving LDS at launch (lds_reserve).
 constexpr int kScoreMfmaRing = 4;
 constexpr int kScoreWgsPerCu = 4;
-constexpr int kLdsPerCu = 160 * 1024;
 
 // Matrix-core form of score_kernel for HI a multiple of 4: the same lanes,
 // loads and fused multiply-adds in the same order, issued as
@@ -293,7 +291,7 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t s) {
     // the query staging (qs) is the kernel's only LDS; the rest of the
     // workgroup's share is reserved to cap residency
     constexpr int staged = DI * HI * 4;
-    constexpr int reserve = kLdsPerCu / kScoreWgsPerCu - staged;
+    constexpr int reserve = lds_reserve(kScoreWgsPerCu, staged);
     static_assert(reserve >= 0, "query staging exceeds the workgroup's LDS share");
     hipLaunchKernelGGL((score_mfma_kernel<HI, DI>), grid, dim3(kScoreWaves * kWave), reserve, s,
                        a.index_q, a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0,
