@@ -52,10 +52,12 @@ struct TileLoader {
 // Stores of a wavefront's 64 scores (lane l: group g) and of its tile's four
 // 16-group segment maxima (mk: the maximum order key of the lane's DPP row),
 // the maxima as one 16-byte store from lane 0; segments past the row's last
-// group hold 0 there, and are never read.  Both are nontemporal: in a
+// group hold 0 there, and are never read.  The scores are nontemporal: in a
 // load-only probe of this kernel's reads, plain 256-byte score stores per
 // wavefront added 5-10 us to the 163 us read of 1 GiB, nontemporal ones about
-// 1 us (in the decode step the gain is 0-4 us, depending on the device).
+// 1 us (in the decode step the gain is 0-4 us, depending on the device).  The
+// maxima (a sixteenth of the bytes) are plain stores, which the selection
+// reads first: about 1 us less per decode step than nontemporal ones.
 __device__ __forceinline__ void store_scores(float* __restrict__ srow, uint32_t* __restrict__ mrow,
                                              int64_t g_max, int64_t g, bool ok, float s,
                                              uint32_t mk) {
@@ -69,7 +71,7 @@ __device__ __forceinline__ void store_scores(float* __restrict__ srow, uint32_t*
     typedef int v4i __attribute__((ext_vector_type(4)));
     if (lane == 0 && ok)
       __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)mk, (int)m1, (int)m2, (int)m3}, mrs,
-                                             (int)((g / kSegment) * 4), 0, kPolicyNt);
+                                             (int)((g / kSegment) * 4), 0, 0);
   }
 }
 
