@@ -212,10 +212,10 @@ QSA_API int qsa_resolve_gather(const qsa_shape *shape, const int32_t *token_ids,
 /* Step 8: F32 online softmax attention over the width compact rows of each
  * row, out = softmax(scale * q . k) . v per query head ([SET] §Floating
  * point makes order observable; [MASK] §Decision).  Rows are visited in
- * chronological order in fixed chunks of consecutive rows whose partial
- * (max, denominator, accumulator) states are folded in ascending chunk
- * order (one state per range of consecutive chunks, the range states then
- * merged in ascending order), so results depend on the width alone and are
+ * chronological order in fixed slices of consecutive rows whose online
+ * softmax states (max, denominator, accumulator) are folded in ascending
+ * order, one state per range of consecutive rows, the range states then
+ * merged in ascending order, so results depend on the width alone and are
  * run-to-run bit-identical.  width 0 gives out = +0
  * and lse = -inf.  lse may be NULL. */
 QSA_API int qsa_online_attend(const qsa_shape *shape, const float *q, const float *k_compact,

@@ -4,31 +4,31 @@
 // arithmetic; in F32 the visit order shows in the last bits, so one canonical
 // order is fixed (AFN-017 "Top-k chooses the set; time chooses the order",
 // §Floating point makes order observable).  The order used here depends on
-// the width alone: the compact row is cut into chunks of kAttnChunk
-// consecutive rows; each chunk produces a partial (max m_c, denominator l_c,
-// accumulator acc_c) with a fixed butterfly for the denominator and a
-// chronological accumulation over the chunk's rows; the partials of each
-// range of kAttnRange consecutive chunks are folded in ascending chunk order
-// into one range partial (running maximum, rescale, denominator and
-// accumulator updates), and the range partials are merged the same way in
-// ascending range order.  No float atomics: results are run-to-run identical.
+// the width alone.  The compact row is cut into chunks of kAttnChunk
+// consecutive rows and the chunks into ranges of kAttnRange.  Within a range,
+// each of four row slices of a chunk (16 rows) belongs to one wavefront,
+// which keeps an online-softmax state per query head over its slices of the
+// range's chunks in ascending order: running maximum, weights exp(s - m),
+// rescale of the weight sum (a fixed butterfly per chunk) and of the
+// accumulators (a chronological accumulation over the slice's rows) when the
+// maximum grows.  At the range's end the four states are rescaled to the
+// range maximum and added in wavefront order: one partial (max, denominator,
+// accumulator) per range, and the range partials are merged the same way in
+// ascending range order.  No float atomics: results are run-to-run
+// identical.
 //
 // attend_chunk_kernel: a persistent workgroup walks its (range, KV head, row)
-// items chunk by chunk, keeping the range's running partial in registers and
-// storing it after the range's last chunk, so the merge reads one partial
-// per range instead of one per chunk.  Each chunk serves every
-// query head of the KV head's GQA group (query head hq reads KV head
-// hq / (H_q/H_kv)).  Scores: the chunk's K rows and query heads are staged
-// in LDS; wavefront w scores rows 16w..16w+15 for every head of the group on
-// v_mfma_f32_16x16x4_f32 (one column per head); the per-head chunk maximum is
-// exchanged once between the wavefronts (the maxima and sums over a
-// wavefront's four lane rows use the VALU cross-lane swaps, the merge's DPP
-// row rotations).  P.V: wavefront w accumulates rows
-// [w*C/NW, (w+1)*C/NW) in row order with lane = output dimension, reading its
-// V rows straight from memory (issued before the score phase); the NW
-// partial sums are then added in wavefront order.  The chunk's accumulation
-// order is therefore fixed by the chunk alone.  merge_kernel: four
-// wavefronts per (query head, row).
+// items chunk by chunk and stores a range's partial after its last chunk, so
+// the merge reads one partial per range.  Each chunk serves every query head
+// of the KV head's GQA group (query head hq reads KV head hq / (H_q/H_kv)).
+// Scores: the chunk's K rows and query heads are staged in LDS; wavefront w
+// scores rows 16w..16w+15 for every head of the group on
+// v_mfma_f32_16x16x4_f32 (one column per head); the maxima and sums over a
+// wavefront's four lane rows use the VALU cross-lane swaps.  P.V: wavefront w
+// accumulates its rows in row order with lane = output dimension, reading its
+// V rows straight from memory (issued before the score phase).  The
+// wavefronts meet only at the K staging and at range ends: two barriers per
+// chunk.  merge_kernel: four wavefronts per (query head, row).
 #include <atomic>
 
 #include "qsa_internal.h"
@@ -367,15 +367,15 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
   load_q(cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, cn, 0);
-  // the range's running partial for this thread's outputs
-  float4 racc[OV4];
-  float rm[OV4], rl[OV4];
+  // this wavefront's running softmax state over the chunks of the current
+  // range: per head, the maximum and weight sum over its rows so far (lane
+  // (li, lq) tracks head li) and the P.V accumulators (lane = dimensions)
+  float m_run = -INFINITY, l_run = 0.0f;
+  float acc[GQ][DPL];
 #pragma unroll
-  for (int r = 0; r < OV4; ++r) {
-    racc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    rm[r] = -INFINITY;
-    rl[r] = 0.0f;
-  }
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) acc[h][t] = 0.0f;
   while (pcur.it < items) {
     const Pos pnx = advance(pcur);
     const Pos pnx2 = advance(pnx);
@@ -445,8 +445,10 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         sp[1] = mfma4(a4.w, b4.w, sp[1]);
       }
       const f32x4 sacc = sp[0] + sp[1];
-      // softmax: the chunk maximum per head from the four wavefronts' maxima
-      // over their 16 rows, then this wavefront's weights and their sum
+      // softmax, per wavefront: the running maximum per head over this
+      // wavefront's rows of the range so far (no exchange between wavefronts
+      // until the range ends); the accumulators and the weight sum so far are
+      // rescaled by alpha = exp(m_old - m_new)
       const int rbase = 16 * wave + 4 * lq;  // rows rbase .. rbase+3 in this lane
       float sc[4];
       float mx = -INFINITY;
@@ -457,32 +459,32 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       }
       mx = xor16(mx, MaxOp{});  // over the four lane rows: lq = 0..3
       mx = xor32(mx, MaxOp{});
-      if (lq == 0 && hcol) mw_sh[wave][li] = mx;
       resolve_slots(nxt2, cn_next2);
-      __syncthreads();  // maxima exchanged; K no longer read, so smem can hold partials
+      const float m_new = fmaxf(m_run, mx);
+      // a head with no row so far keeps alpha = 1 (its state is all zeros)
+      const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run - m_new);
       {
         const int h = hcol ? li : 0;
-        float m = mw_sh[0][h];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) m = fmaxf(m, mw_sh[w][h]);
         float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = rbase + r < cn ? expf(sc[r] - m) : 0.0f;
+        for (int r = 0; r < 4; ++r) p[r] = rbase + r < cn ? expf(sc[r] - m_new) : 0.0f;
         float l = ((p[0] + p[1]) + p[2]) + p[3];
         l = xor16(l, AddOp{});
         l = xor32(l, AddOp{});
-        if (hcol) {
-          ps4[(h * C + rbase) / 4] = make_float4(p[0], p[1], p[2], p[3]);  // read back below
-          if (lq == 0) lw_sh[wave][h] = l;                                   // by this wavefront
-        }
+        l_run = l_run * alpha + l;
+        m_run = m_new;
+        if (hcol) ps4[(h * C + rbase) / 4] = make_float4(p[0], p[1], p[2], p[3]);  // read back below
       }
 
-      // P.V over this wavefront's rows, in row order; lane owns dims lane*DPL..
-      float acc[GQ][DPL];
+      // P.V over this wavefront's rows, in row order, onto the rescaled
+      // running accumulators; lane owns dims lane*DPL..  (alpha of head h is
+      // lane h's)
 #pragma unroll
-      for (int h = 0; h < GQ; ++h)
+      for (int h = 0; h < GQ; ++h) {
+        const float ah = read_lane(alpha, h);
 #pragma unroll
-        for (int t = 0; t < DPL; ++t) acc[h][t] = 0.0f;
+        for (int t = 0; t < DPL; ++t) acc[h][t] = acc[h][t] * ah;
+      }
       // head-major, one head's weights live at a time (the scheduling barrier
       // keeps the compiler from hoisting every head's LDS reads at once)
 #pragma unroll
@@ -506,60 +508,61 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       __builtin_amdgcn_sched_barrier(0);
       load_v(nxt, cn_next, rs_next);
 
-      // combine the wavefronts' partial sums in wavefront order
-#pragma unroll
-      for (int h = 0; h < GQ; ++h)
-#pragma unroll
-        for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
-      __syncthreads();
-      // fold this chunk's partial into the range's (online rescale: running
-      // maximum, weights exp(m - m')), and store it after the range's last chunk
+      // at the range's last chunk: the wavefronts' states are exchanged,
+      // rescaled to the range maximum and added in wavefront order, and the
+      // range partial is stored; the state then restarts
       const int64_t slot0 =
           (cur.lrow * q_heads + (int64_t)cur.hk * GQ) * n_ranges + cur.chunk / RC;
       const bool range_end = pnx.sub == 0;
-      if (cn > 0) {
+      if (range_end) {
+        __syncthreads();  // every wavefront is done reading K: smem can hold the states
 #pragma unroll
-        for (int r = 0; r < OV4; ++r) {
-          const int o4 = tid + r * NT;
-          if (o4 < GQ * D / 4) {
-            const int h = (4 * o4) / D;
-            const int d = 4 * o4 - h * D;
-            float4 sum = smem4[(h * D + d) / 4];
+        for (int h = 0; h < GQ; ++h)
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) {
-              const float4 t = smem4[((ww * GQ + h) * D + d) / 4];
-              sum.x = sum.x + t.x;
-              sum.y = sum.y + t.y;
-              sum.z = sum.z + t.z;
-              sum.w = sum.w + t.w;
-            }
-            float mc = mw_sh[0][h];
+          for (int t = 0; t < DPL; ++t) smem[(wave * GQ + h) * D + lane * DPL + t] = acc[h][t];
+        if (lq == 0 && hcol) {
+          mw_sh[wave][li] = m_run;
+          lw_sh[wave][li] = l_run;
+        }
+        __syncthreads();
+        if (cn > 0) {
 #pragma unroll
-            for (int w = 1; w < NW; ++w) mc = fmaxf(mc, mw_sh[w][h]);
-            const float lc = (lw_sh[0][h] + lw_sh[1][h]) + (lw_sh[2][h] + lw_sh[3][h]);
-            if (pcur.sub == 0) {
-              racc[r] = sum;
-              rm[r] = mc;
-              rl[r] = lc;
-            } else {
-              const float mn = fmaxf(rm[r], mc);
-              const float a = expf(rm[r] - mn), b = expf(mc - mn);
-              racc[r].x = racc[r].x * a + sum.x * b;
-              racc[r].y = racc[r].y * a + sum.y * b;
-              racc[r].z = racc[r].z * a + sum.z * b;
-              racc[r].w = racc[r].w * a + sum.w * b;
-              rl[r] = rl[r] * a + lc * b;
-              rm[r] = mn;
-            }
-            if (range_end) {
-              *reinterpret_cast<float4*>(part_acc + (slot0 + (int64_t)h * n_ranges) * D + d) =
-                  racc[r];
+          for (int r = 0; r < OV4; ++r) {
+            const int o4 = tid + r * NT;
+            if (o4 < GQ * D / 4) {
+              const int h = (4 * o4) / D;
+              const int d = 4 * o4 - h * D;
+              float mc = mw_sh[0][h];
+#pragma unroll
+              for (int w = 1; w < NW; ++w) mc = fmaxf(mc, mw_sh[w][h]);
+              float ew[NW];
+#pragma unroll
+              for (int w = 0; w < NW; ++w) ew[w] = expf(mw_sh[w][h] - mc);
+              const float4 t0 = smem4[(h * D + d) / 4];
+              float4 sum = make_float4(t0.x * ew[0], t0.y * ew[0], t0.z * ew[0], t0.w * ew[0]);
+              float lc = lw_sh[0][h] * ew[0];
+#pragma unroll
+              for (int ww = 1; ww < NW; ++ww) {
+                const float4 t = smem4[((ww * GQ + h) * D + d) / 4];
+                sum.x = __builtin_fmaf(t.x, ew[ww], sum.x);
+                sum.y = __builtin_fmaf(t.y, ew[ww], sum.y);
+                sum.z = __builtin_fmaf(t.z, ew[ww], sum.z);
+                sum.w = __builtin_fmaf(t.w, ew[ww], sum.w);
+                lc = __builtin_fmaf(lw_sh[ww][h], ew[ww], lc);
+              }
+              *reinterpret_cast<float4*>(part_acc + (slot0 + (int64_t)h * n_ranges) * D + d) = sum;
               if (d == 0)
                 *reinterpret_cast<float2*>(part_ml + (slot0 + (int64_t)h * n_ranges) * 2) =
-                    make_float2(rm[r], rl[r]);
+                    make_float2(mc, lc);
             }
           }
         }
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h)
+#pragma unroll
+          for (int t = 0; t < DPL; ++t) acc[h][t] = 0.0f;
       }
       resolve_store(FUSED ? (j + 2) % 3 : 0, cn_next2);  // visible after the next item's first barrier
     }
