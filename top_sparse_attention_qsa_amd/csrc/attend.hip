@@ -26,7 +26,9 @@
 // v_mfma_f32_16x16x4_f32 (one column per head); the maxima and sums over a
 // wavefront's four lane rows use the VALU cross-lane swaps.  P.V: wavefront w
 // accumulates its rows in row order with lane = output dimension, reading its
-// V rows straight from memory (issued before the score phase).  The
+// V rows straight from memory (issued before the score phase), on
+// v_mfma_f32_4x4x1_16b_f32 when the group has a multiple of four heads (one
+// product per step, the bits of the VALU fused multiply-adds).  The
 // wavefronts meet only at the K staging and at range ends: two barriers per
 // chunk.  merge_kernel: four wavefronts per (query head, row).
 #include <atomic>
@@ -485,23 +487,61 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
 #pragma unroll
         for (int t = 0; t < DPL; ++t) acc[h][t] = acc[h][t] * ah;
       }
-      // head-major, one head's weights live at a time (the scheduling barrier
-      // keeps the compiler from hoisting every head's LDS reads at once)
+      if constexpr (GQ % 4 == 0) {
+        // on v_mfma_f32_4x4x1_16b_f32: block b (lanes 4b..4b+3) adds A[i] *
+        // B[j] to D[i][j] with one rounding, A[i] from lane 4b+i, B[j] from
+        // lane 4b+j, D[i][j] in register i of lane 4b+j.  With A = the weight
+        // of head 4hq + (lane mod 4) for the row and B = the lane's V value,
+        // register i of lane l accumulates head 4hq + i at the lane's own
+        // dimensions: the same fused multiply-adds, in the same row order, as
+        // on the VALU, so the same bits
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        const int pi = lane & 3;
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        float4 p4[KPW / 4];
+        for (int hq = 0; hq < GQ / 4; ++hq) {
+          v4f pacc[DPL];
 #pragma unroll
-        for (int j4 = 0; j4 < KPW / 4; ++j4) p4[j4] = ps4[(h * C + wave * KPW) / 4 + j4];
+          for (int t = 0; t < DPL; ++t)
+            pacc[t] = v4f{acc[4 * hq][t], acc[4 * hq + 1][t], acc[4 * hq + 2][t], acc[4 * hq + 3][t]};
+          float4 p4[KPW / 4];
 #pragma unroll
-        for (int j4 = 0; j4 < KPW / 4; ++j4) {
-          const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
+          for (int j4 = 0; j4 < KPW / 4; ++j4)
+            p4[j4] = ps4[((4 * hq + pi) * C + wave * KPW) / 4 + j4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
+          for (int j4 = 0; j4 < KPW / 4; ++j4) {
+            const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
 #pragma unroll
-            for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
-              acc[h][t] = __builtin_fmaf(pv[jj], vreg[4 * j4 + jj][t], acc[h][t]);
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+              for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
+                pacc[t] = __builtin_amdgcn_mfma_f32_4x4x1f32(pv[jj], vreg[4 * j4 + jj][t], pacc[t],
+                                                             0, 0, 0);
+          }
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+            for (int t = 0; t < DPL; ++t) acc[4 * hq + i2][t] = pacc[t][i2];
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // head-major, one head's weights live at a time (the scheduling barrier
+        // keeps the compiler from hoisting every head's LDS reads at once)
+  #pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          float4 p4[KPW / 4];
+  #pragma unroll
+          for (int j4 = 0; j4 < KPW / 4; ++j4) p4[j4] = ps4[(h * C + wave * KPW) / 4 + j4];
+  #pragma unroll
+          for (int j4 = 0; j4 < KPW / 4; ++j4) {
+            const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+  #pragma unroll
+              for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
+                acc[h][t] = __builtin_fmaf(pv[jj], vreg[4 * j4 + jj][t], acc[h][t]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_q(nxt);  // the next item's query heads, then its V, stream in under the rest
