@@ -158,8 +158,8 @@ def build_probe():
 
 def context_bandwidth(reps=10):
     """Achievable-bandwidth context, not a denominator of anything reported:
-    a plain streaming read of 1 GiB (bench_stream_read.hip, grid-stride
-    float4 loads) and torch's device copy of 1 GiB."""
+    reads of 1 GiB (bench_stream_read.hip: grid-stride float4 loads, and the
+    scoring kernel's tiled shape) and torch's device copy of 1 GiB."""
     import ctypes
     import torch
     n = (1 << 30) // 4
@@ -171,14 +171,17 @@ def context_bandwidth(reps=10):
     if not os.path.exists(PROBE_LIB):
         build_probe()
     bw = ctypes.CDLL(PROBE_LIB)
-    bw.bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                  ctypes.c_void_p]
+    for f in (bw.bw_stream_read, bw.bw_tiled_read):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
 
-    def read():
-        s = torch.cuda.current_stream().cuda_stream
-        if bw.bw_stream_read(x.data_ptr(), 4 * n, sink.data_ptr(), s) != 0:
-            raise RuntimeError("bw_stream_read failed")
-    fns.insert(0, ("stream_read", read, 4 * n))
+    def reader(f):
+        def read():
+            s = torch.cuda.current_stream().cuda_stream
+            if f(x.data_ptr(), 4 * n, sink.data_ptr(), s) != 0:
+                raise RuntimeError("bandwidth probe failed")
+        return read
+    fns.insert(0, ("tiled_read", reader(bw.bw_tiled_read), 4 * n))
+    fns.insert(0, ("stream_read", reader(bw.bw_stream_read), 4 * n))
     for name, fn, nbytes in fns:
         for _ in range(3):
             fn()
@@ -194,8 +197,10 @@ def context_bandwidth(reps=10):
         res[f"{name}_gbps"] = nbytes / (ms * 1e-3) / 1e9
     del x, y
     torch.cuda.empty_cache()
-    res["note"] = ("1 GiB of f32: a grid-stride streaming read kernel, and torch's device copy "
-                   "(bytes read + written); context only")
+    res["note"] = ("1 GiB of f32: a grid-stride streaming read kernel, a read in the scoring "
+                   "kernel's tiled shape (32 KiB per wavefront, four 1 KiB loads in flight, five "
+                   "workgroups per compute unit), and torch's device copy (bytes read + written); "
+                   "context only")
     return res
 
 
