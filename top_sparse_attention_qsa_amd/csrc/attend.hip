@@ -32,6 +32,7 @@
 // wavefronts meet only at the K staging and at range ends: two barriers per
 // chunk.  merge_kernel: four wavefronts per (query head, row).
 #include <atomic>
+#include <type_traits>
 
 #include "qsa_internal.h"
 
@@ -241,11 +242,12 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
           row_ptr(src.k_compact, src.k_cache, x, ic, ring_slot) + 4 * c);
     }
   };
-  auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
+  auto load_v_rows = [&](const Item& x, int cn_raw, int ring_slot, auto J0, auto J1) {
+    constexpr int j0 = decltype(J0)::value, j1 = decltype(J1)::value;
     if constexpr (MODE == kCompact) {
       const auto rs = item_rsrc(src.v_compact, x, cn_raw);
 #pragma unroll
-      for (int j = 0; j < KPW; ++j) {
+      for (int j = j0; j < j1; ++j) {
         const int i = wave * KPW + j;
         if constexpr (DPL == 2) {
           const f32x2 v = __builtin_bit_cast(
@@ -261,7 +263,7 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
     }
     const int cn = cn_raw > 0 ? cn_raw : 1;
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
+    for (int j = j0; j < j1; ++j) {
       const int i = wave * KPW + j;
       const int ic = i < cn ? i : cn - 1;
       const float* vp = row_ptr(src.v_compact, src.v_cache, x, ic, ring_slot);
@@ -273,6 +275,10 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         vreg[j][0] = vp[lane];
       }
     }
+  };
+  auto load_v = [&](const Item& x, int cn_raw, int ring_slot) {
+    load_v_rows(x, cn_raw, ring_slot, std::integral_constant<int, 0>{},
+                std::integral_constant<int, KPW>{});
   };
   // Fused resolution of item x in three phases on wavefront 0, lane i = row i:
   // IDs loaded (before the next item's K loads, so that waiting for them
@@ -494,35 +500,52 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
         // of head 4hq + (lane mod 4) for the row and B = the lane's V value,
         // register i of lane l accumulates head 4hq + i at the lane's own
         // dimensions: the same fused multiply-adds, in the same row order, as
-        // on the VALU, so the same bits
+        // on the VALU, so the same bits.  Rows go in quads; once a quad is
+        // done for every head its V registers are refilled with the next
+        // chunk's rows, so those loads start a part of P.V earlier.
         typedef float v4f __attribute__((ext_vector_type(4)));
         const int pi = lane & 3;
+        v4f pacc[GQ / 4][DPL];
 #pragma unroll
-        for (int hq = 0; hq < GQ / 4; ++hq) {
-          v4f pacc[DPL];
+        for (int hq = 0; hq < GQ / 4; ++hq)
 #pragma unroll
           for (int t = 0; t < DPL; ++t)
-            pacc[t] = v4f{acc[4 * hq][t], acc[4 * hq + 1][t], acc[4 * hq + 2][t], acc[4 * hq + 3][t]};
-          float4 p4[KPW / 4];
+            pacc[hq][t] = v4f{acc[4 * hq][t], acc[4 * hq + 1][t], acc[4 * hq + 2][t],
+                              acc[4 * hq + 3][t]};
+        load_q(nxt);  // the next item's query heads stream in under P.V
+        __builtin_amdgcn_sched_barrier(0);
+        auto quad = [&](auto J4) {
+          constexpr int j4 = decltype(J4)::value;
+          float4 p4[GQ / 4];
 #pragma unroll
-          for (int j4 = 0; j4 < KPW / 4; ++j4)
-            p4[j4] = ps4[((4 * hq + pi) * C + wave * KPW) / 4 + j4];
+          for (int hq = 0; hq < GQ / 4; ++hq)
+            p4[hq] = ps4[((4 * hq + pi) * C + wave * KPW) / 4 + j4];
 #pragma unroll
-          for (int j4 = 0; j4 < KPW / 4; ++j4) {
-            const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
+          for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
+            for (int hq = 0; hq < GQ / 4; ++hq) {
+              const float pv = jj == 0 ? p4[hq].x : jj == 1 ? p4[hq].y : jj == 2 ? p4[hq].z : p4[hq].w;
 #pragma unroll
               for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
-                pacc[t] = __builtin_amdgcn_mfma_f32_4x4x1f32(pv[jj], vreg[4 * j4 + jj][t], pacc[t],
-                                                             0, 0, 0);
-          }
+                pacc[hq][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(pv, vreg[4 * j4 + jj][t],
+                                                                 pacc[hq][t], 0, 0, 0);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+          load_v_rows(nxt, cn_next, rs_next, std::integral_constant<int, 4 * j4>{},
+                      std::integral_constant<int, 4 * j4 + 4>{});
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        static_assert(KPW == 16, "four row quads per wavefront");
+        quad(std::integral_constant<int, 0>{});
+        quad(std::integral_constant<int, 1>{});
+        quad(std::integral_constant<int, 2>{});
+        quad(std::integral_constant<int, 3>{});
+#pragma unroll
+        for (int hq = 0; hq < GQ / 4; ++hq)
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2)
 #pragma unroll
-            for (int t = 0; t < DPL; ++t) acc[4 * hq + i2][t] = pacc[t][i2];
-          __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int t = 0; t < DPL; ++t) acc[4 * hq + i2][t] = pacc[hq][t][i2];
       } else {
         // head-major, one head's weights live at a time (the scheduling barrier
         // keeps the compiler from hoisting every head's LDS reads at once)
@@ -543,10 +566,12 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      load_q(nxt);  // the next item's query heads, then its V, stream in under the rest
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(nxt, cn_next, rs_next);
+      if constexpr (GQ % 4 != 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_q(nxt);  // the next item's query heads, then its V, stream in under the rest
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(nxt, cn_next, rs_next);
+      }
 
       // at the range's last chunk: the wavefronts' states are exchanged,
       // rescaled to the range maximum and added in wavefront order, and the
