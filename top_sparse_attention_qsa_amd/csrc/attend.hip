@@ -549,17 +549,17 @@ attend_chunk_kernel(const float* __restrict__ q, RowSource src, const int32_t* _
       } else {
         // head-major, one head's weights live at a time (the scheduling barrier
         // keeps the compiler from hoisting every head's LDS reads at once)
-  #pragma unroll
+#pragma unroll
         for (int h = 0; h < GQ; ++h) {
           float4 p4[KPW / 4];
-  #pragma unroll
+#pragma unroll
           for (int j4 = 0; j4 < KPW / 4; ++j4) p4[j4] = ps4[(h * C + wave * KPW) / 4 + j4];
-  #pragma unroll
+#pragma unroll
           for (int j4 = 0; j4 < KPW / 4; ++j4) {
             const float pv[4] = {p4[j4].x, p4[j4].y, p4[j4].z, p4[j4].w};
-  #pragma unroll
+#pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-  #pragma unroll
+#pragma unroll
               for (int t = 0; t < DPL; ++t)  // rows past the width carry p = 0
                 acc[h][t] = __builtin_fmaf(pv[jj], vreg[4 * j4 + jj][t], acc[h][t]);
           }
