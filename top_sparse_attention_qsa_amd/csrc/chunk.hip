@@ -44,7 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // the compiler takes enough registers that only two fit, and the MFMA pipes
 // idle while they wait for B (measured 25% slower at 16 heads x 128).
 // Smaller index shapes hold more rows per workgroup and keep the default.
-template <int HI, int DI>
+template <int HI, int DI, bool CERT>
 __global__ void __launch_bounds__(4 * kWave)
 __attribute__((amdgpu_waves_per_eu(HI * DI >= 512 ? 3 : 2)))
 chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ pooled,
@@ -64,18 +64,26 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   const int lane = lane_id();
   const int64_t lrow0 = (int64_t)blockIdx.x * RB;  // first local row of this workgroup
   const int64_t grow0 = row0 + lrow0;
-  const int b = (int)(grow0 / queries);            // all RB rows share this sequence
+  // all RB rows share one sequence (RB divides the queries per sequence and
+  // the first row); rows fit in 32 bits (at most 65,535), so one 32-bit
+  // division finds it
+  const int32_t b = (int32_t)grow0 / queries;
+  const int32_t j0 = (int32_t)grow0 - b * queries;  // query index of the first row
+  const int64_t n0 = (int64_t)seq_len[b] - queries + 1 + j0;  // visible tokens of the first row
 
   // the longest row of the workgroup sets the tile range; shorter rows mask.
   // A workgroup whose four tiles all lie past it leaves before staging
   // anything (with rows of very different lengths, most of the grid).
+  // Row r sees n0 + r tokens (a row with none or more than g_max groups has
+  // no groups to score).
   int64_t g_rows[RB];
   int64_t g_max_rows = 0;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    const RowView rv = row_view(seq_len, grow0 + r, queries, g_max);
-    g_rows[r] = rv.valid ? rv.g : -1;
-    g_max_rows = rv.g > g_max_rows && rv.valid ? rv.g : g_max_rows;
+    const int64_t n = n0 + r;
+    const bool valid = n >= 0 && (n >> 2) <= g_max;
+    g_rows[r] = valid ? (n >> 2) : -1;
+    g_max_rows = valid && (n >> 2) > g_max_rows ? (n >> 2) : g_max_rows;
   }
   if ((int64_t)blockIdx.y * 4 * 64 >= g_max_rows) return;
 
@@ -177,8 +185,17 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   constexpr float gD = DI * u / (1.0f - DI * u);
   constexpr float gD2 = (DI + 2) * u / (1.0f - (DI + 2) * u);
   constexpr float gH = HI * u / (1.0f - HI * u);
+  // After the head sum, lane (li, lq) holds for every N-subtile t the score
+  // of group 16t + li for query row m * RPM + sub_row; the CPR lane groups
+  // of one row hold copies.  The stores give each copy its own subtiles:
+  // store v of M-tile m writes subtile t = v * CPR + lq % CPR, so every lane
+  // writes a distinct group and a DPP row holds one 16-group segment
+  // (4 / CPR stores per M-tile, all lanes active; at 16 heads one store
+  // writes the tile's 64 groups as 256 contiguous bytes).
+  constexpr int CPR = HI / 4;
   const int sub_row = (4 * (lane >> 4)) / HI;  // row within the M-tile held by this lane
-  float wt[4] = {0.0f, 0.0f, 0.0f, 0.0f};      // per M-tile: the widest group of the tile
+  const int copy = (lane >> 4) % CPR;
+  float knorm[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     // |k_g|^2: lanes l, l^16, l^32, l^48 hold the four k-lanes of group l%16
@@ -186,58 +203,64 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
     float kk = ksq[t];
     kk = xor16(kk, AddOp{});
     kk = xor32(kk, AddOp{});
-    const float knorm = sqrtf(kk);
-    const int64_t g = tile * 64 + t * 16 + (lane & 15);
+    knorm[t] = sqrtf(kk);
+  }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < 4; ++m) {
+    const int r = m * RPM + sub_row;
+    int64_t g_row = g_rows[m * RPM];  // select, not a lane-dependent register index
+#pragma unroll
+    for (int q2 = 1; q2 < RPM; ++q2)
+      if (sub_row == q2) g_row = g_rows[m * RPM + q2];
+    const int64_t lr = lrow0 + r;
+    float sv[4], ev[4];
+    float wt = 0.0f;  // the widest group of this lane's four (row, tile) groups
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
       // D[4*(l/16) + r][l%16]: this lane's four M-rows, all of one query row
       const f32x4 d = acc[m][t];
       float s = (d.x > 0.f ? d.x : 0.f) + (d.y > 0.f ? d.y : 0.f) + (d.z > 0.f ? d.z : 0.f) +
                 (d.w > 0.f ? d.w : 0.f);
       if constexpr (HI >= 8) s = xor16(s, AddOp{});  // the head sum across lane rows
       if constexpr (HI >= 16) s = xor32(s, AddOp{});
-      const int r = m * RPM + sub_row;
-      int64_t g_row = g_rows[m * RPM];  // select, not a lane-dependent register index
-#pragma unroll
-      for (int q2 = 1; q2 < RPM; ++q2)
-        if (sub_row == q2) g_row = g_rows[m * RPM + q2];
-      const float e = 2.0f * (((2.0f * gD2 + gD) * knorm * qnorm[r] + 2.0f * gH * fabsf(s)) /
+      const float e = 2.0f * (((2.0f * gD2 + gD) * knorm[t] * qnorm[r] + 2.0f * gH * fabsf(s)) /
                               (1.0f - gH)) + 1e-30f;
-      const bool ok = g < g_row;
-      // one lane group per query row writes (the others hold copies)
-      const bool writer = ((lane >> 4) % (HI / 4)) == 0;
-      const int64_t lr = lrow0 + r;
-      if (ok && writer) {
-        if (approx) approx[lr * g_max + g] = s;
-        if (bound) bound[lr * g_max + g] = e;
-        if (hi) hi[lr * g_max + g] = s + e;
-      }
-      if (lo_maxima) {
-        // segment = the 16 lanes of a DPP row
-        const uint32_t mk = row_max16_u32(ok ? order_key(s - e) : 0u);
-        if (writer && (lane & 15) == 0 && ok)
-          lo_maxima[lr * (g_max / kSegment) + g / kSegment] = mk;
-      }
+      sv[t] = s;
+      ev[t] = e;
+      const int64_t g = tile * 64 + t * 16 + (lane & 15);
       // hi - s <= (s~ + e)(1 + u) - (s~ - e/2) < 1.5e + u|hi|; the width adds
       // margin for its own rounding and for the subtraction hi - W the
       // selection makes, so that fl(hi - W) <= s (select.hip, certified band)
-      if (ok) wt[m] = fmaxf(wt[m], 2.02f * e + 4.0f * u * fabsf(s + e));
+      if (CERT && g < g_row) wt = fmaxf(wt, 2.02f * e + 4.0f * u * fabsf(s + e));
     }
-  }
-  if (widths) {
-    // one width per (row, 64-group tile): the maximum over the DPP row of the
-    // lanes' maxima over the four N-subtiles (all 64 groups of the tile)
-    const bool writer = ((lane >> 4) % (HI / 4)) == 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float w = row_max16(wt[m]);
-      const int r = m * RPM + sub_row;
-      int64_t g_row = g_rows[m * RPM];
+    for (int v = 0; v < 4 / CPR; ++v) {
+      const int t = v * CPR + copy;
+      float s = sv[v * CPR], e = ev[v * CPR];
 #pragma unroll
-      for (int q2 = 1; q2 < RPM; ++q2)
-        if (sub_row == q2) g_row = g_rows[m * RPM + q2];
-      if (writer && (lane & 15) == 0 && tile * 64 < g_row)
-        widths[(lrow0 + r) * (g_max / 64) + tile] = w;
+      for (int c = 1; c < CPR; ++c)
+        if (copy == c) {
+          s = sv[v * CPR + c];
+          e = ev[v * CPR + c];
+        }
+      const int64_t g = tile * 64 + t * 16 + (lane & 15);
+      const bool ok = g < g_row;
+      if constexpr (CERT) {
+        if (ok) hi[lr * g_max + g] = s + e;
+        // segment = the 16 lanes of a DPP row
+        const uint32_t mk = row_max16_u32(ok ? order_key(s - e) : 0u);
+        if ((lane & 15) == 0 && ok) lo_maxima[lr * (g_max / kSegment) + g / kSegment] = mk;
+      } else if (ok) {
+        approx[lr * g_max + g] = s;
+        bound[lr * g_max + g] = e;
+      }
+    }
+    if constexpr (CERT) {
+      // one width per (row, 64-group tile): the maximum over the DPP row of the
+      // lanes' maxima over the four N-subtiles (all 64 groups of the tile)
+      const float w = row_max16(wt);
+      if (copy == 0 && (lane & 15) == 0 && tile * 64 < g_row)
+        widths[lr * (g_max / 64) + tile] = w;
     }
   }
 }
@@ -245,12 +268,21 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
 template <int HI, int DI>
 hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t s) {
   constexpr int RB = 4 * (16 / HI);
+  const bool cert = a.hi != nullptr;
+  if (cert ? (!a.lo_maxima || !a.widths || a.approx || a.bound)
+           : (!a.approx || !a.bound || a.lo_maxima || a.widths))
+    return hipErrorInvalidValue;
   const int64_t tiles = (a.g_max + 63) / 64;
   dim3 grid((unsigned)(a.rows / RB), (unsigned)((tiles + 3) / 4));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_score_kernel<HI, DI>), grid, dim3(4 * kWave), 0, s, a.index_q,
-                     a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0, a.approx,
-                     a.bound, a.hi, a.lo_maxima, a.widths);
+  if (cert)
+    hipLaunchKernelGGL((chunk_score_kernel<HI, DI, true>), grid, dim3(4 * kWave), 0, s,
+                       a.index_q, a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0,
+                       a.approx, a.bound, a.hi, a.lo_maxima, a.widths);
+  else
+    hipLaunchKernelGGL((chunk_score_kernel<HI, DI, false>), grid, dim3(4 * kWave), 0, s,
+                       a.index_q, a.pooled, a.pooled_off, a.seq_len, a.queries, a.g_max, a.row0,
+                       a.approx, a.bound, a.hi, a.lo_maxima, a.widths);
   return hipGetLastError();
 }
 

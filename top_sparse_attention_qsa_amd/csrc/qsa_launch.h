@@ -136,12 +136,14 @@ struct ChunkArgs {
   int64_t g_max;
   int64_t row0;
   int64_t rows;              // a multiple of 4*16/H_I
-  float* approx;             // [rows][g_max] approximate scores, may be null
-  float* bound;              // [rows][g_max] certified error bounds, may be null
-  float* hi;                 // [rows][g_max] approx + bound, may be null
-  uint32_t* lo_maxima;       // [rows][g_max/16] order keys of approx - bound, may be null
+  // two output sets: approx and bound, or hi, lo_maxima and widths (the
+  // pointers of the other set null; any other combination is refused)
+  float* approx;             // [rows][g_max] approximate scores
+  float* bound;              // [rows][g_max] certified error bounds
+  float* hi;                 // [rows][g_max] approx + bound
+  uint32_t* lo_maxima;       // [rows][g_max/16] order keys of approx - bound
   float* widths = nullptr;   // [rows][g_max/64] per 64-group tile, an upper bound of
-                             // hi - s over its groups (s: the chain score), may be null
+                             // hi - s over its groups (s: the chain score)
 };
 
 // Exact rescoring inputs for the certified selection (chunk rows).
