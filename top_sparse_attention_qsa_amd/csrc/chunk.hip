@@ -56,7 +56,6 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   constexpr int RB = 4 * RPM;     // query rows per workgroup
   constexpr int NQ = DI / 16;     // quads of four k-steps
   __shared__ f32x4 qa[NQ * 4 * kWave];  // A fragments [quad][M-tile][lane], 4 k-steps each
-  __shared__ float hnorm[RB * HI];      // |q_(row, head)|
   __shared__ float qnorm[RB];           // sum over heads of |q_h| per row
 
   const int tid = (int)threadIdx.x;
@@ -90,41 +89,39 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   // stage A fragments: A[i][kk] of M-tile m, k-step 4q + s = q[row][head][16q + 4kk + s]
   // with M-row i -> (row m*RPM + i/HI, head i%HI), i = lane%16, kk = lane/16.
   // Each thread moves NQ float4s (four consecutive dimensions each), all
-  // loads issued before the first store.
+  // loads issued before the first store.  Thread (wavefront m, lane l) moves
+  // quad n's float4 of M-tile m, lane l: its NQ float4s are a quarter of one
+  // (row, head) pair's dimensions, the lanes l, l^16, l^32, l^48 hold the
+  // rest, so the norms come from the same registers.
   {
     f32x4 st[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-      const int f = tid + n * 4 * kWave;  // (quad * 4 + M-tile) * 64 + lane
-      const int l = f & (kWave - 1);
-      const int m = (f >> 6) & 3;
-      const int i = l & 15;
-      const int r = m * RPM + i / HI;
+      const int i = lane & 15;
+      const int r = wave * RPM + i / HI;
       st[n] = *reinterpret_cast<const f32x4*>(
-          index_q + ((grow0 + r) * HI + (i % HI)) * DI + 16 * (f >> 8) + 4 * (l >> 4));
+          index_q + ((grow0 + r) * HI + (i % HI)) * DI + 16 * n + 4 * (lane >> 4));
     }
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) qa[tid + n * 4 * kWave] = st[n];
-  }
-  __syncthreads();
-  if (tid < RB * HI) {  // (row, head) pair tid = M-tile tid/16, M-row tid%16 (RB * HI == 64)
     float ss = 0.0f;
-    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const f32x4 v = qa[(q * 4 + (tid >> 4)) * kWave + kk * 16 + (tid & 15)];
-        ss = __builtin_fmaf(v.x, v.x, ss);
-        ss = __builtin_fmaf(v.y, v.y, ss);
-        ss = __builtin_fmaf(v.z, v.z, ss);
-        ss = __builtin_fmaf(v.w, v.w, ss);
-      }
-    hnorm[tid] = sqrtf(ss);
-  }
-  __syncthreads();
-  if (tid < RB) {
-    float sn = 0.0f;
-    for (int h = 0; h < HI; ++h) sn += hnorm[tid * HI + h];
-    qnorm[tid] = sn;
+    for (int n = 0; n < NQ; ++n) {
+      qa[tid + n * 4 * kWave] = st[n];
+      ss = __builtin_fmaf(st[n].x, st[n].x, ss);
+      ss = __builtin_fmaf(st[n].y, st[n].y, ss);
+      ss = __builtin_fmaf(st[n].z, st[n].z, ss);
+      ss = __builtin_fmaf(st[n].w, st[n].w, ss);
+    }
+    ss = xor16(ss, AddOp{});  // the pair's four quarters
+    ss = xor32(ss, AddOp{});
+    // |q_(row, head)| summed over the row's HI heads: aligned groups of HI
+    // lanes of a DPP row, by quad swaps and row mirrors (each step adds two
+    // partial sums whose order does not matter, so all lanes agree)
+    float sn = sqrtf(ss);
+    if constexpr (HI >= 2) sn = sn + dpp_f32<0xB1>(sn);   // quad_perm [1,0,3,2]
+    if constexpr (HI >= 4) sn = sn + dpp_f32<0x4E>(sn);   // quad_perm [2,3,0,1]
+    if constexpr (HI >= 8) sn = sn + dpp_f32<0x141>(sn);  // row_half_mirror
+    if constexpr (HI >= 16) sn = sn + dpp_f32<0x140>(sn); // row_mirror
+    if (lane < 16 && lane % HI == 0) qnorm[wave * RPM + lane / HI] = sn;
   }
   __syncthreads();
 
