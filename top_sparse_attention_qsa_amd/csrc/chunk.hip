@@ -15,7 +15,8 @@
 // rounding-error bound of an n-term sum, once for the MFMA order, allowing an
 // extra rounding per product, and once for the chain; sum_d |q_d k_d| is
 // bounded by Cauchy-Schwarz; ReLU is 1-Lipschitz; the final 2 absorbs the
-// rounding of E itself).  The kernel writes hi = s~ + E as the row's score,
+// rounding of E itself: a few operations of at most an ulp each, the square
+// roots on the hardware's v_sqrt_f32 and 1/(1 - g(H)) a rounded constant).  The kernel writes hi = s~ + E as the row's score,
 // the per-16-group maxima of the order key of lo = s~ - E, and per 64-group
 // tile a width W >= hi - s.  The selection kernel keeps every group whose hi
 // reaches a lower bound of the k-th largest lo, settles by their bounds which
@@ -116,7 +117,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
     // |q_(row, head)| summed over the row's HI heads: aligned groups of HI
     // lanes of a DPP row, by quad swaps and row mirrors (each step adds two
     // partial sums whose order does not matter, so all lanes agree)
-    float sn = sqrtf(ss);
+    float sn = __builtin_amdgcn_sqrtf(ss);
     if constexpr (HI >= 2) sn = sn + dpp_f32<0xB1>(sn);   // quad_perm [1,0,3,2]
     if constexpr (HI >= 4) sn = sn + dpp_f32<0x4E>(sn);   // quad_perm [2,3,0,1]
     if constexpr (HI >= 8) sn = sn + dpp_f32<0x141>(sn);  // row_half_mirror
@@ -182,6 +183,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   constexpr float gD = DI * u / (1.0f - DI * u);
   constexpr float gD2 = (DI + 2) * u / (1.0f - (DI + 2) * u);
   constexpr float gH = HI * u / (1.0f - HI * u);
+  constexpr float kInvOneMinusGH = 1.0f / (1.0f - gH);
   // After the head sum, lane (li, lq) holds for every N-subtile t the score
   // of group 16t + li for query row m * RPM + sub_row; the CPR lane groups
   // of one row hold copies.  The stores give each copy its own subtiles:
@@ -200,7 +202,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
     float kk = ksq[t];
     kk = xor16(kk, AddOp{});
     kk = xor32(kk, AddOp{});
-    knorm[t] = sqrtf(kk);
+    knorm[t] = __builtin_amdgcn_sqrtf(kk);
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -220,8 +222,8 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
                 (d.w > 0.f ? d.w : 0.f);
       if constexpr (HI >= 8) s = xor16(s, AddOp{});  // the head sum across lane rows
       if constexpr (HI >= 16) s = xor32(s, AddOp{});
-      const float e = 2.0f * (((2.0f * gD2 + gD) * knorm[t] * qnorm[r] + 2.0f * gH * fabsf(s)) /
-                              (1.0f - gH)) + 1e-30f;
+      const float e = 2.0f * (((2.0f * gD2 + gD) * knorm[t] * qnorm[r] + 2.0f * gH * fabsf(s)) *
+                              kInvOneMinusGH) + 1e-30f;
       sv[t] = s;
       ev[t] = e;
       const int64_t g = tile * 64 + t * 16 + (lane & 15);
