@@ -87,6 +87,20 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   }
   if ((int64_t)blockIdx.y * 4 * 64 >= g_max_rows) return;
 
+  // this wavefront's pooled-key tile; a wavefront whose tile lies past the
+  // rows reads tile 0 (which exists: the workgroup has a tile inside) until
+  // it leaves after the barrier, so no load sits behind a branch
+  const int64_t tile = (int64_t)blockIdx.y * 4 + wave;
+  const bool active = tile * 64 < g_max_rows;
+  const float* __restrict__ kt = pooled + pooled_off[b] + (active ? tile : 0) * (64 * DI);
+  // lane (kk, j) of N-subtile t, quad q reads dimensions 16q + 4kk .. +3 of group 16t + j
+  const float* __restrict__ kl = kt + (lane >> 4) * 256 + (lane & 15) * 4;
+  auto load_quad = [&](f32x4 (&dst)[4], int q) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t] = *reinterpret_cast<const f32x4*>(kl + q * 1024 + t * 64);
+  };
+  f32x4 b0[4], b1[4];
+
   // stage A fragments: A[i][kk] of M-tile m, k-step 4q + s = q[row][head][16q + 4kk + s]
   // with M-row i -> (row m*RPM + i/HI, head i%HI), i = lane%16, kk = lane/16.
   // Each thread moves NQ float4s (four consecutive dimensions each), all
@@ -103,6 +117,11 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
       st[n] = *reinterpret_cast<const f32x4*>(
           index_q + ((grow0 + r) * HI + (i % HI)) * DI + 16 * n + 4 * (lane >> 4));
     }
+    // the first quad of B is issued after the A loads, so that waiting for
+    // A does not wait for it, and arrives while A is staged
+    __builtin_amdgcn_sched_barrier(0);
+    load_quad(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     float ss = 0.0f;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
@@ -126,22 +145,14 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   }
   __syncthreads();
 
-  const int64_t tile = (int64_t)blockIdx.y * 4 + wave;
-  if (tile * 64 >= g_max_rows) return;
+  if (!active) return;
 
-  const float* __restrict__ kt = pooled + pooled_off[b] + tile * (64 * DI);
   f32x4 acc[4][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ksq[4] = {0.f, 0.f, 0.f, 0.f};
-  // lane (kk, j) of N-subtile t, quad q reads dimensions 16q + 4kk .. +3 of group 16t + j
-  const float* __restrict__ kl = kt + (lane >> 4) * 256 + (lane & 15) * 4;
-  auto load_quad = [&](f32x4 (&dst)[4], int q) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dst[t] = *reinterpret_cast<const f32x4*>(kl + q * 1024 + t * 64);
-  };
   auto run_quad = [&](const f32x4 (&bv)[4], int q) {
     f32x4 a[4];
 #pragma unroll
@@ -165,8 +176,6 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
   };
   // two-deep ring over quads (NQ is even); the last refill re-reads the last
   // quad instead of being conditional, so every wait is for the older quad only
-  f32x4 b0[4], b1[4];
-  load_quad(b0, 0);
 #pragma unroll 1
   for (int q = 0; q < NQ; q += 2) {
     load_quad(b1, q + 1);
