@@ -41,6 +41,11 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// v_sqrt_f32 is within an ulp for arguments from 2^-96 up; smaller sums of
+// squares are raised to 2^-96 first, which can only enlarge a norm, so the
+// bound stays an upper bound.
+constexpr float kSqrtFloor = 0x1p-96f;
+
 // At least three wavefronts per SIMD: without the register limit this sets,
 // the compiler takes enough registers that only two fit, and the MFMA pipes
 // idle while they wait for B (measured 25% slower at 16 heads x 128).
@@ -136,7 +141,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
     // |q_(row, head)| summed over the row's HI heads: aligned groups of HI
     // lanes of a DPP row, by quad swaps and row mirrors (each step adds two
     // partial sums whose order does not matter, so all lanes agree)
-    float sn = __builtin_amdgcn_sqrtf(ss);
+    float sn = __builtin_amdgcn_sqrtf(fmaxf(ss, kSqrtFloor));
     if constexpr (HI >= 2) sn = sn + dpp_f32<0xB1>(sn);   // quad_perm [1,0,3,2]
     if constexpr (HI >= 4) sn = sn + dpp_f32<0x4E>(sn);   // quad_perm [2,3,0,1]
     if constexpr (HI >= 8) sn = sn + dpp_f32<0x141>(sn);  // row_half_mirror
@@ -211,7 +216,7 @@ chunk_score_kernel(const float* __restrict__ index_q, const float* __restrict__ 
     float kk = ksq[t];
     kk = xor16(kk, AddOp{});
     kk = xor32(kk, AddOp{});
-    knorm[t] = __builtin_amdgcn_sqrtf(kk);
+    knorm[t] = __builtin_amdgcn_sqrtf(fmaxf(kk, kSqrtFloor));
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
