@@ -106,6 +106,35 @@ def test_chunk_tie_heavy_grid_duplicates():
     assert_same(case, decode_per_row(case))
 
 
+def test_chunk_bounds_hold_for_tiny_keys():
+    """Keys scaled by 2^-56 and queries by 2^56 (exact scalings: the products,
+    and so the chain scores, are those of the unscaled inputs): the keys' sums
+    of squares fall below 2^-96, where the kernel raises them before the
+    hardware square root; the bound must still hold for every group."""
+    h_i, d_i, q = 16, 128, 16
+    spec = inputs.custom("bounds_tiny", [3000, 9000], queries=q, h_i=h_i, d_i=d_i, h_q=2,
+                         h_kv=1, d=64, budget=64)
+    data = inputs.make(spec, seed=11, device="cpu")
+    data["raw_keys"] = data["raw_keys"] * 2.0 ** -56
+    data["index_q"] = data["index_q"] * 2.0 ** 56
+    case = harness.GpuCase(data)
+    sh = case.shape
+    approx = torch.full((spec.rows, sh.max_groups), float("nan"), device="cuda")
+    bound = torch.full_like(approx, float("nan"))
+    qsa.qsa_score_groups_chunk(sh, case.index_q, case.pooled, case.pooled_off, case.seq_len,
+                               approx, bound)
+    approx, bound = approx.cpu().numpy(), bound.cpu().numpy()
+    for r in range(spec.rows):
+        n = inputs.row_tokens(spec, r)
+        off = int(data["raw_off"][r // q])
+        pooled = oracle.pool_full(data["raw_keys"][off:off + n].numpy())
+        assert float(np.max(np.sum(pooled.astype(np.float64) ** 2, axis=1))) < 2.0 ** -96
+        exact = oracle.score(data["index_q"][r].numpy(), pooled)
+        g = len(exact)
+        err = np.abs(approx[r, :g].astype(np.float64) - exact)
+        assert np.all(err <= bound[r, :g]), r
+
+
 def test_chunk_all_tied_streaming_path():
     """Zero index queries: every bound is 0 and every score +0, so the candidate
     buffer overflows and exact keys are streamed; groups 0..k-1 must win."""
