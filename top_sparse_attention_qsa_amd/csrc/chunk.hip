@@ -33,7 +33,9 @@
 // 4q + kk of the tiled layout), and 16 lanes read 256 contiguous bytes.  A
 // fragments are staged in LDS once per workgroup in the same order, one
 // float4 per (quad, M-tile, lane).  The B loads of quad q + 1 are in flight
-// while quad q runs on MFMA.
+// while quad q runs on MFMA.  The output set is a template parameter (CERT):
+// approximate scores and bounds, or hi, lo maxima and tile widths for the
+// certified selection.
 #include "qsa_internal.h"
 
 namespace qsa {
