@@ -63,8 +63,9 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
   // four workgroups per compute unit: 0.941 ms against 0.982 ms for the eight
   // that fit by threads (4 GiB read, 1 GiB written; three to five per compute
   // unit did about as well, six or more no better than eight)
-  hipLaunchKernelGGL(pool_kernel<DI>, grid, dim3(256), lds_reserve(kPoolWgsPerCu, 0), s, a.raw_keys, a.raw_off, a.seq_len,
-                     a.first_group, a.pooled, a.pooled_off, a.g_max);
+  hipLaunchKernelGGL(pool_kernel<DI>, grid, dim3(256), lds_reserve(kPoolWgsPerCu, 0), s,
+                     a.raw_keys, a.raw_off, a.seq_len, a.first_group, a.pooled, a.pooled_off,
+                     a.g_max);
   return hipGetLastError();
 }
 
