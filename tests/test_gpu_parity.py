@@ -219,7 +219,7 @@ def test_dense_parity_sweep():
 
 @pytest.mark.parametrize("h_i,d_i,h_q,h_kv,d", [
     (1, 32, 2, 2, 64), (2, 64, 4, 1, 128), (4, 128, 16, 1, 64), (16, 32, 16, 16, 128),
-    (8, 128, 8, 2, 64), (4, 64, 16, 1, 128)])
+    (8, 128, 8, 2, 64), (4, 64, 16, 1, 128), (4, 32, 8, 1, 64), (2, 32, 2, 1, 128)])
 def test_shapes_ragged_batch_small_budget(h_i, d_i, h_q, h_kv, d):
     lens = [0, 3, 63, 64, 65, 257, 1000, 4097]
     spec = inputs.custom("ragged", lens, h_i=h_i, d_i=d_i, h_q=h_q, h_kv=h_kv, d=d, budget=16,
@@ -337,7 +337,8 @@ def test_fused_equals_compact(named):
 
 
 @pytest.mark.parametrize("h_i,d_i,h_q,h_kv,d", [(1, 32, 2, 2, 64), (4, 128, 16, 1, 64),
-                                                (16, 32, 16, 16, 128)])
+                                                (16, 32, 16, 16, 128), (2, 64, 8, 1, 64),
+                                                (8, 32, 4, 2, 128)])
 def test_fused_ragged_shapes(h_i, d_i, h_q, h_kv, d):
     lens = [0, 3, 63, 64, 65, 257, 1000, 4097]
     spec = inputs.custom("ragged_f", lens, h_i=h_i, d_i=d_i, h_q=h_q, h_kv=h_kv, d=d, budget=16,
